@@ -1,0 +1,166 @@
+"""Pins that tie the CPU oracle to facts fixed outside its own code.
+
+Each ``pin_*`` function takes a loaded oracle library (so the mutation test
+can run the same pins against deliberately broken builds of the oracle) and
+raises AssertionError when the oracle disagrees with:
+
+* hand-computed products (tests/golden/hand_products.txt);
+* the exact rational product (Python ``fractions``), within the double
+  rounding bound K * 2**-53 * sum|a b|, on every shape up to 4 x 4 x 4 and a
+  few larger ragged ones, with NaN-filled leading-dimension padding;
+* closed forms: A * I = A and I * B = B exactly; B = ones gives row sums of A;
+* a library routine on a case that reduces to it: integer inputs make the
+  product exact, equal to numpy's int64 matrix product;
+* degenerate sizes: K = 0 gives zeros, M = 0 or N = 0 gives an empty result.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from roofline_sgemm_f32_amd.inputs import as_numpy, make_operands
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_hand_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "hand_products.txt")) as f:
+        lines = [ln.split("#")[0].strip() for ln in f]
+    lines = [ln for ln in lines if ln]
+    i = 0
+    while i < len(lines):
+        head = lines[i].split()
+        assert head[0] == "case", head
+        name, M, N, K = head[1], int(head[2]), int(head[3]), int(head[4])
+        i += 1
+        rows = [[float(v) for v in lines[i + r].split()] for r in range(M + K + M)]
+        i += M + K + M
+        A = np.array(rows[:M], dtype=np.float32).reshape(M, K)
+        B = np.array(rows[M:M + K], dtype=np.float32).reshape(K, N)
+        C = np.array(rows[M + K:], dtype=np.float64).reshape(M, N)
+        cases.append((name, A, B, C))
+    return cases
+
+
+def exact_product(A: np.ndarray, B: np.ndarray):
+    """Exact rational A*B and sum|a b|, element by element."""
+    M, K = A.shape
+    N = B.shape[1]
+    Af = [[Fraction(float(A[i, k])) for k in range(K)] for i in range(M)]
+    Bf = [[Fraction(float(B[k, j])) for j in range(N)] for k in range(K)]
+    C = [[sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0)) for j in range(N)]
+         for i in range(M)]
+    S = [[sum((abs(Af[i][k] * Bf[k][j]) for k in range(K)), Fraction(0)) for j in range(N)]
+         for i in range(M)]
+    return C, S
+
+
+def _assert_close_exact(name, got, got_S, C, S, K):
+    M = len(C)
+    N = len(C[0]) if M else 0
+    tol_scale = max(K, 1) * 2.0 ** -53
+    for i in range(M):
+        for j in range(N):
+            tol = float(S[i][j]) * tol_scale
+            assert abs(Fraction(float(got[i, j])) - C[i][j]) <= Fraction(tol), \
+                f"{name}: C[{i},{j}]={got[i, j]!r} exact={float(C[i][j])!r}"
+            if got_S is not None:
+                assert abs(Fraction(float(got_S[i, j])) - S[i][j]) <= Fraction(tol), \
+                    f"{name}: S[{i},{j}]={got_S[i, j]!r} exact={float(S[i][j])!r}"
+
+
+def pin_hand_examples(lib):
+    for name, A, B, C in load_hand_cases():
+        got, S = oracle.sgemm_f64(A, B, lib=lib, threads=2)
+        assert np.array_equal(got, C), f"{name}: {got} != {C}"
+        rows, _ = oracle.sgemm_rows_f64(A, B, np.arange(A.shape[0]), lib=lib, threads=2)
+        assert np.array_equal(rows, C), f"{name} (rows): {rows} != {C}"
+        ii, jj = np.meshgrid(np.arange(A.shape[0]), np.arange(B.shape[1]), indexing="ij")
+        ent, _ = oracle.sgemm_entries_f64(A, B, ii.ravel(), jj.ravel(), lib=lib)
+        assert np.array_equal(ent.reshape(C.shape), C), f"{name} (entries)"
+
+
+def _shapes_small():
+    for M in range(1, 5):
+        for N in range(1, 5):
+            for K in range(1, 5):
+                yield M, N, K
+    yield from [(5, 7, 3), (3, 2, 9), (6, 5, 17), (2, 9, 33)]
+
+
+def pin_bruteforce_exact(lib):
+    for t, (M, N, K) in enumerate(_shapes_small()):
+        # Leading dimensions with NaN padding catch any read past a row.
+        A, B = make_operands(M, N, K, "uniform", seed=1000 + t, lda=K + (t % 3), ldb=N + (t % 2))
+        A, B = as_numpy(A), as_numpy(B)
+        C, S = exact_product(A, B)
+        got, got_S = oracle.sgemm_f64(A, B, lib=lib, threads=3)
+        _assert_close_exact(f"full {M}x{N}x{K}", got, got_S, C, S, K)
+        rows = np.arange(M)[::-1].copy()
+        gr, gs = oracle.sgemm_rows_f64(A, B, rows, lib=lib, threads=2)
+        _assert_close_exact(f"rows {M}x{N}x{K}", gr, gs, [C[r] for r in rows],
+                            [S[r] for r in rows], K)
+        ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ge, gse = oracle.sgemm_entries_f64(A, B, ii.ravel(), jj.ravel(), lib=lib)
+        _assert_close_exact(f"entries {M}x{N}x{K}", ge.reshape(M, N), gse.reshape(M, N), C, S, K)
+
+
+def pin_identity(lib):
+    A, B = make_operands(19, 23, 11, "uniform", seed=7)
+    A, B = as_numpy(A), as_numpy(B)
+    I_k = np.eye(11, dtype=np.float32)
+    got, _ = oracle.sgemm_f64(A, I_k, lib=lib)  # A * I = A
+    assert np.array_equal(got, A.astype(np.float64)), "A*I != A"
+    got, _ = oracle.sgemm_f64(I_k, B, lib=lib)  # I * B = B
+    assert np.array_equal(got, B.astype(np.float64)), "I*B != B"
+
+
+def pin_all_ones(lib):
+    # B = ones: every entry of row i is the sum of row i of A.
+    A, _ = make_operands(13, 1, 57, "uniform", seed=8)
+    A = as_numpy(A)
+    ones = np.ones((57, 9), dtype=np.float32)
+    got, S = oracle.sgemm_f64(A, ones, lib=lib)
+    for i in range(13):
+        exact = math.fsum(float(v) for v in A[i])
+        tol = 57 * 2.0 ** -53 * float(np.abs(A[i].astype(np.float64)).sum())
+        assert np.all(np.abs(got[i] - exact) <= tol), f"row {i} sum"
+    # A = ones: every entry of column j is the sum of column j of B.
+    _, B = make_operands(1, 12, 40, "int", seed=9)
+    B = as_numpy(B)
+    got, _ = oracle.sgemm_f64(np.ones((5, 40), dtype=np.float32), B, lib=lib)
+    colsum = B.astype(np.int64).sum(axis=0)
+    assert np.array_equal(got, np.tile(colsum, (5, 1)).astype(np.float64)), "column sums"
+
+
+def pin_integer_library(lib):
+    # Integer inputs in [-2, 2]: the product is an exact small integer, so it
+    # must equal numpy's exact int64 product bit for bit.
+    for (M, N, K, lda, ldb) in [(37, 29, 41, 41, 29), (64, 65, 63, 70, 66), (1, 200, 300, 300, 201)]:
+        A, B = make_operands(M, N, K, "int", seed=M * 7 + N, lda=lda, ldb=ldb)
+        A, B = as_numpy(A), as_numpy(B)
+        want = np.matmul(A.astype(np.int64), B.astype(np.int64))
+        want_abs = np.matmul(np.abs(A.astype(np.int64)), np.abs(B.astype(np.int64)))
+        got, S = oracle.sgemm_f64(A, B, lib=lib, threads=4)
+        assert np.array_equal(got, want.astype(np.float64)), f"int {M}x{N}x{K}"
+        assert np.array_equal(S, want_abs.astype(np.float64)), f"int bound {M}x{N}x{K}"
+
+
+def pin_degenerate(lib):
+    A = np.zeros((4, 0), dtype=np.float32)
+    B = np.zeros((0, 6), dtype=np.float32)
+    got, S = oracle.sgemm_f64(A, B, lib=lib)
+    assert got.shape == (4, 6) and np.all(got == 0) and np.all(S == 0), "K=0 must give zeros"
+    got, _ = oracle.sgemm_f64(np.zeros((0, 3), np.float32), np.ones((3, 5), np.float32), lib=lib)
+    assert got.shape == (0, 5)
+    got, _ = oracle.sgemm_f64(np.ones((2, 3), np.float32), np.zeros((3, 0), np.float32), lib=lib)
+    assert got.shape == (2, 0)
+
+
+ALL_PINS = [pin_hand_examples, pin_bruteforce_exact, pin_identity, pin_all_ones,
+            pin_integer_library, pin_degenerate]
