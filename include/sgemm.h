@@ -1,0 +1,125 @@
+/*
+ * sgemm.h - C ABI of the MI355X (gfx950) single-precision matrix multiply.
+ *
+ * Operation (amittech.dev, "3.5 Project: tiled matrix multiplication",
+ * sections "the numeric background" and "starter scaffolding"): for
+ * row-major float matrices, C = A * B, i.e.
+ *
+ *     C[i*ldc + j] = sum_{k<K} A[i*lda + k] * B[k*ldb + j],   0<=i<M, 0<=j<N,
+ *
+ * costing 2*M*N*K floating-point operations.  The page works with square
+ * N x N matrices and asks the code to accept any N; this interface takes the
+ * general M x K by K x N shape with BLAS-style leading dimensions.  C is
+ * overwritten and never read (the course's library call passes alpha = 1 and
+ * beta = 0; section "the reference ceiling").  Accumulation is in float.
+ *
+ * Shapes and layout
+ *   M, N, K >= 0.  M == 0 or N == 0: nothing is done and SGEMM_OK returned.
+ *   K == 0: C (M x N) is set to zero.
+ *   lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N); elements between a
+ *   row's end and the next row's start are neither read (A, B) nor written
+ *   (C).  Pointers need only 4-byte alignment; 16-byte alignment with lda,
+ *   ldb, K and N multiples of 4 selects wider loads internally.
+ *
+ * Ownership and concurrency
+ *   A, B and C are device pointers owned by the caller (for example the data
+ *   of torch tensors).  The library allocates no device memory, keeps no
+ *   per-call state and is reentrant.  The work is enqueued on ``stream``
+ *   (a hipStream_t; NULL means the null stream) and the call returns without
+ *   synchronising; a device fault surfaces at the caller's next
+ *   synchronisation.
+ *
+ * Errors
+ *   Arguments are validated on the host before any HIP call; a bad argument
+ *   returns a nonzero sgemm_status_t and enqueues nothing.  A failed launch
+ *   returns SGEMM_ERR_LAUNCH; sgemm_last_hip_error() then gives the HIP error
+ *   code of the calling thread's last failure.  The library never exits or
+ *   aborts the process.
+ */
+#ifndef SGEMM_MI355X_H
+#define SGEMM_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel ladder.  Every variant computes the same product and accepts every
+ * shape the validation above accepts; they differ in how they use the chip.
+ * Variants 0-4 are the ladder proper; 5-7 are comparison points. */
+typedef enum sgemm_variant {
+    SGEMM_AUTO = 0,              /* pick per shape (the matrix-core kernel for large shapes) */
+    SGEMM_K1_COALESCED = 1,      /* one output per lane, lanes along a row of C (coalesced B/C, uniform A) */
+    SGEMM_K2_LDS_TILED = 2,      /* 32 x 32 LDS tiles of A and B per K step, padded rows; one output per lane */
+    SGEMM_K3_REGTILE_DB = 3,     /* 128 x 128 workgroup tile, 8 x 8 outputs per lane in VGPRs, LDS double buffer */
+    SGEMM_K4_MFMA = 4,           /* FP32 matrix-core kernel (v_mfma_f32_32x32x2_f32), direct global->LDS loads */
+    SGEMM_K2_LDS_TILED16 = 5,    /* as K2 with 16 x 16 tiles */
+    SGEMM_K2_LDS_TILED_NOPAD = 6,/* as K2 with unpadded 32 x 32 tiles (LDS bank-conflict comparison) */
+    SGEMM_K0_NAIVE = 7,          /* one output per lane, lanes down a column of C (uncoalesced foil) */
+    SGEMM_VARIANT_COUNT = 8
+} sgemm_variant_t;
+
+typedef enum sgemm_status {
+    SGEMM_OK = 0,
+    SGEMM_ERR_DIM = 1,         /* a negative M, N or K */
+    SGEMM_ERR_LD = 2,          /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+    SGEMM_ERR_NULLPTR = 3,     /* a NULL operand that the shape requires */
+    SGEMM_ERR_VARIANT = 4,     /* unknown variant */
+    SGEMM_ERR_ALIAS = 5,       /* C's byte range overlaps A's or B's */
+    SGEMM_ERR_LAUNCH = 6,      /* the HIP launch failed (see sgemm_last_hip_error) */
+    SGEMM_ERR_UNSUPPORTED = 7, /* the explicit variant cannot index this shape (AUTO always can) */
+    SGEMM_ERR_ARG = 8          /* another invalid argument (copy probe: n < 0, bad block or grid) */
+} sgemm_status_t;
+
+/* C = A * B with the variant chosen per shape.  Same as
+ * sgemm_f32_variant(SGEMM_AUTO, ...). */
+int sgemm_f32(int64_t M, int64_t N, int64_t K,
+              const float *A, int64_t lda,
+              const float *B, int64_t ldb,
+              float *C, int64_t ldc, void *stream);
+
+/* C = A * B with an explicit ladder variant (sgemm_variant_t). */
+int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K,
+                      const float *A, int64_t lda,
+                      const float *B, int64_t ldb,
+                      float *C, int64_t ldc, void *stream);
+
+/* Device-to-device copy dst[i] = src[i], 0 <= i < n, with a grid-stride loop:
+ * the HBM bandwidth probe of amittech.dev, "7.3 Bandwidths and peak rate -
+ * exercises", exercise 2 (it moves 2 * n * 4 bytes).  dst and src are device
+ * pointers owned by the caller and must not overlap (SGEMM_ERR_ALIAS).
+ * n == 0 does nothing.  Default launch shape. */
+int sgemm_copy_f32(float *dst, const float *src, int64_t n, void *stream);
+
+/* The same copy with an explicit launch shape, for the exercise's block and
+ * grid sweep: block is the workgroup size (a multiple of 64, 64..1024), grid
+ * the number of workgroups (1..2^20).  Invalid values give SGEMM_ERR_ARG. */
+int sgemm_copy_f32_launch(float *dst, const float *src, int64_t n,
+                          int block, int64_t grid, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *sgemm_status_string(int status);
+
+/* Static name of a variant ("auto", "k1_coalesced", ...), or NULL if unknown. */
+const char *sgemm_variant_name(int variant);
+
+/* The variant SGEMM_AUTO would run for this shape and these pointers
+ * (host-only decision, no HIP call). */
+int sgemm_auto_variant(int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float *C, int64_t ldc);
+
+/* hipError_t of the calling thread's last SGEMM_ERR_LAUNCH (0 if none). */
+int sgemm_last_hip_error(void);
+
+/* ABI version of this header (incremented on incompatible change). */
+int sgemm_abi_version(void);
+
+#define SGEMM_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_MI355X_H */

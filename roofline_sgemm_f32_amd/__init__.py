@@ -1,1 +1,14 @@
-"""MI355X (gfx950) single-precision dense matrix multiply, C = A * B."""
+"""MI355X (gfx950) single-precision dense matrix multiply, C = A * B.
+
+The compute path is a C-ABI shared library of hand-written HIP kernels
+(``libsgemm.so``, declared in ``include/sgemm.h``); ``binding`` is a thin
+ctypes layer over it.  Importing the package does not load the library; the
+first call does, and raises if it is missing.
+"""
+from .binding import (EXPORTS, STATUS, VARIANTS, SgemmError, copy_f32, copy_f32_launch,
+                      library_path, load, sgemm, sgemm_f32, sgemm_f32_variant, status_string,
+                      variant_name)
+
+__all__ = ["EXPORTS", "STATUS", "VARIANTS", "SgemmError", "copy_f32", "copy_f32_launch",
+           "library_path", "load", "sgemm", "sgemm_f32", "sgemm_f32_variant", "status_string",
+           "variant_name"]

@@ -1,0 +1,170 @@
+"""ctypes binding over libsgemm.so (declared in include/sgemm.h).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  PyTorch supplies device memory and the stream.  If the library
+has not been built, the first call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libsgemm.so")
+_lib = None
+
+# sgemm_variant_t
+VARIANTS = {
+    "auto": 0,
+    "k1_coalesced": 1,
+    "k2_lds_tiled32": 2,
+    "k3_regtile_db": 3,
+    "k4_mfma": 4,
+    "k2_lds_tiled16": 5,
+    "k2_lds_tiled32_nopad": 6,
+    "k0_naive": 7,
+}
+
+# sgemm_status_t
+STATUS = {
+    0: "SGEMM_OK", 1: "SGEMM_ERR_DIM", 2: "SGEMM_ERR_LD", 3: "SGEMM_ERR_NULLPTR",
+    4: "SGEMM_ERR_VARIANT", 5: "SGEMM_ERR_ALIAS", 6: "SGEMM_ERR_LAUNCH",
+    7: "SGEMM_ERR_UNSUPPORTED", 8: "SGEMM_ERR_ARG",
+}
+
+EXPORTS = ["sgemm_f32", "sgemm_f32_variant", "sgemm_copy_f32", "sgemm_copy_f32_launch",
+           "sgemm_status_string", "sgemm_variant_name", "sgemm_auto_variant",
+           "sgemm_last_hip_error", "sgemm_abi_version"]
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libsgemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m roofline_sgemm_f32_amd.build`"
+                           " (there is no non-HIP fallback)")
+    lib = ctypes.CDLL(p)
+    i64, vp, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    gemm = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.sgemm_f32.argtypes = gemm
+    lib.sgemm_f32.restype = cint
+    lib.sgemm_f32_variant.argtypes = [cint, *gemm]
+    lib.sgemm_f32_variant.restype = cint
+    lib.sgemm_copy_f32.argtypes = [vp, vp, i64, vp]
+    lib.sgemm_copy_f32.restype = cint
+    lib.sgemm_copy_f32_launch.argtypes = [vp, vp, i64, cint, i64, vp]
+    lib.sgemm_copy_f32_launch.restype = cint
+    lib.sgemm_status_string.argtypes = [cint]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_variant_name.argtypes = [cint]
+    lib.sgemm_variant_name.restype = ctypes.c_char_p
+    lib.sgemm_auto_variant.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64]
+    lib.sgemm_auto_variant.restype = cint
+    lib.sgemm_last_hip_error.argtypes = []
+    lib.sgemm_last_hip_error.restype = cint
+    lib.sgemm_abi_version.argtypes = []
+    lib.sgemm_abi_version.restype = cint
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().sgemm_status_string(int(status)).decode()
+
+
+def variant_name(variant: int) -> str | None:
+    r = load().sgemm_variant_name(int(variant))
+    return r.decode() if r is not None else None
+
+
+def _variant_id(variant) -> int:
+    if isinstance(variant, str):
+        if variant not in VARIANTS:
+            raise ValueError(f"unknown variant {variant!r}; one of {sorted(VARIANTS)}")
+        return VARIANTS[variant]
+    return int(variant)
+
+
+def sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    """Raw entry point: integer pointers and sizes; returns the status code."""
+    return load().sgemm_f32_variant(_variant_id(variant), M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def _ld(t, name):
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    return max(t.stride(0), t.shape[1], 1) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _stream_handle(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def sgemm(A, B, out=None, variant="auto"):
+    """C = A @ B for float32 CUDA (ROCm) tensors, computed by libsgemm on the
+    current stream.  Row-major views with any row stride >= the row length
+    are accepted; ``out`` (M x N, written, never read) may be supplied."""
+    import torch
+    if A.device.type != "cuda" or B.device.type != "cuda":
+        raise ValueError("operands must be GPU tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif out.shape != (M, N):
+        raise ValueError("out has the wrong shape")
+    lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(out, "out")
+    st = sgemm_f32_variant(variant, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                           out.data_ptr(), ldc, _stream_handle(A.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_f32_variant")
+    return out
+
+
+def copy_f32(dst, src):
+    """dst[:] = src[:] (float32 GPU tensors, contiguous) with the copy probe."""
+    n = src.numel()
+    if dst.numel() != n or not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("copy needs contiguous tensors of equal size")
+    st = load().sgemm_copy_f32(dst.data_ptr(), src.data_ptr(), n, _stream_handle(src.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_copy_f32")
+    return dst
+
+
+def copy_f32_launch(dst, src, block: int, grid: int):
+    """The copy probe with an explicit workgroup size and count."""
+    n = src.numel()
+    if dst.numel() != n or not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("copy needs contiguous tensors of equal size")
+    st = load().sgemm_copy_f32_launch(dst.data_ptr(), src.data_ptr(), n, block, grid,
+                                      _stream_handle(src.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_copy_f32_launch")
+    return dst

@@ -1,0 +1,151 @@
+// C ABI entry points: argument validation (host only, before any HIP call),
+// variant dispatch and launch-status reporting.  The interface contract is
+// documented in include/sgemm.h.
+#include "../../include/sgemm.h"
+#include "kernels.h"
+
+using sgemm::GemmArgs;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int launch_status(hipError_t e) {
+    if (e == hipSuccess) return SGEMM_OK;
+    g_last_hip_error = int(e);
+    return SGEMM_ERR_LAUNCH;
+}
+
+// Byte range [lo, hi) spanned by a rows x cols row-major view (rows, cols > 0).
+void span(const void* p, int64_t rows, int64_t cols, int64_t ld, uintptr_t* lo, uintptr_t* hi) {
+    *lo = reinterpret_cast<uintptr_t>(p);
+    *hi = *lo + uintptr_t(((rows - 1) * ld + cols) * int64_t(sizeof(float)));
+}
+
+bool overlaps(uintptr_t alo, uintptr_t ahi, uintptr_t blo, uintptr_t bhi) {
+    return alo < bhi && blo < ahi;
+}
+
+int validate(int variant, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+             const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    if (variant < 0 || variant >= SGEMM_VARIANT_COUNT) return SGEMM_ERR_VARIANT;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+    // Keep every element offset, and (rows - 1) * ld + cols, inside int64.
+    const int64_t lim = int64_t(1) << 40;
+    if (M > lim || N > lim || K > lim) return SGEMM_ERR_DIM;
+    const int64_t k1 = K > 1 ? K : 1, n1 = N > 1 ? N : 1;
+    if (lda < k1 || ldb < n1 || ldc < n1) return SGEMM_ERR_LD;
+    if (lda > lim || ldb > lim || ldc > lim) return SGEMM_ERR_LD;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return SGEMM_ERR_NULLPTR;
+    if (K > 0) {
+        if (A == nullptr || B == nullptr) return SGEMM_ERR_NULLPTR;
+        uintptr_t clo, chi, alo, ahi, blo, bhi;
+        span(C, M, N, ldc, &clo, &chi);
+        span(A, M, K, lda, &alo, &ahi);
+        span(B, K, N, ldb, &blo, &bhi);
+        if (overlaps(clo, chi, alo, ahi) || overlaps(clo, chi, blo, bhi)) return SGEMM_ERR_ALIAS;
+    }
+    return SGEMM_OK;
+}
+
+int choose_auto(const GemmArgs& g) {
+    // The matrix-core kernel handles every shape whose per-slab offsets fit
+    // its 32-bit buffer addressing; the register-tiled kernel (64-bit
+    // offsets) takes the rest.
+    return sgemm::k4_supports(g) ? SGEMM_K4_MFMA : SGEMM_K3_REGTILE_DB;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    const int v = validate(variant, M, N, K, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
+    if (K == 0) return launch_status(sgemm::launch_zero(C, M, N, ldc, s));
+    if (variant == SGEMM_AUTO) variant = choose_auto(g);
+    switch (variant) {
+        case SGEMM_K0_NAIVE: return launch_status(sgemm::launch_k0_naive(g, s));
+        case SGEMM_K1_COALESCED: return launch_status(sgemm::launch_k1_coalesced(g, s));
+        case SGEMM_K2_LDS_TILED: return launch_status(sgemm::launch_k2_lds(g, 32, true, s));
+        case SGEMM_K2_LDS_TILED16: return launch_status(sgemm::launch_k2_lds(g, 16, true, s));
+        case SGEMM_K2_LDS_TILED_NOPAD: return launch_status(sgemm::launch_k2_lds(g, 32, false, s));
+        case SGEMM_K3_REGTILE_DB: return launch_status(sgemm::launch_k3_regtile(g, s));
+        case SGEMM_K4_MFMA:
+            if (!sgemm::k4_supports(g)) return SGEMM_ERR_UNSUPPORTED;
+            return launch_status(sgemm::launch_k4_mfma(g, s));
+        default: return SGEMM_ERR_VARIANT;
+    }
+}
+
+int sgemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+              int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return sgemm_f32_variant(SGEMM_AUTO, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int sgemm_auto_variant(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc) {
+    const int v = validate(SGEMM_AUTO, M, N, K, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return -v;
+    const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
+    return choose_auto(g);
+}
+
+int sgemm_copy_f32_launch(float* dst, const float* src, int64_t n, int block, int64_t grid,
+                          void* stream) {
+    if (n < 0) return SGEMM_ERR_ARG;
+    if (block < 64 || block > 1024 || block % 64 != 0) return SGEMM_ERR_ARG;
+    if (grid < 1 || grid > sgemm::kMaxGrid) return SGEMM_ERR_ARG;
+    if (n == 0) return SGEMM_OK;
+    if (dst == nullptr || src == nullptr) return SGEMM_ERR_NULLPTR;
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+    const uintptr_t bytes = uintptr_t(n) * sizeof(float);
+    if (overlaps(d, d + bytes, s, s + bytes)) return SGEMM_ERR_ALIAS;
+    return launch_status(sgemm::launch_copy(dst, src, n, block, grid,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int sgemm_copy_f32(float* dst, const float* src, int64_t n, void* stream) {
+    const int block = 256;
+    return sgemm_copy_f32_launch(dst, src, n, block, sgemm::copy_default_grid(n, block), stream);
+}
+
+const char* sgemm_status_string(int status) {
+    switch (status) {
+        case SGEMM_OK: return "ok";
+        case SGEMM_ERR_DIM: return "invalid dimension (M, N and K must be >= 0)";
+        case SGEMM_ERR_LD: return "invalid leading dimension (lda >= max(1,K), ldb and ldc >= max(1,N))";
+        case SGEMM_ERR_NULLPTR: return "null operand pointer";
+        case SGEMM_ERR_VARIANT: return "unknown kernel variant";
+        case SGEMM_ERR_ALIAS: return "output overlaps an input";
+        case SGEMM_ERR_LAUNCH: return "kernel launch failed";
+        case SGEMM_ERR_UNSUPPORTED: return "variant cannot address this shape";
+        case SGEMM_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+const char* sgemm_variant_name(int variant) {
+    switch (variant) {
+        case SGEMM_AUTO: return "auto";
+        case SGEMM_K1_COALESCED: return "k1_coalesced";
+        case SGEMM_K2_LDS_TILED: return "k2_lds_tiled32";
+        case SGEMM_K3_REGTILE_DB: return "k3_regtile_db";
+        case SGEMM_K4_MFMA: return "k4_mfma";
+        case SGEMM_K2_LDS_TILED16: return "k2_lds_tiled16";
+        case SGEMM_K2_LDS_TILED_NOPAD: return "k2_lds_tiled32_nopad";
+        case SGEMM_K0_NAIVE: return "k0_naive";
+        default: return nullptr;
+    }
+}
+
+int sgemm_last_hip_error(void) { return g_last_hip_error; }
+
+int sgemm_abi_version(void) { return SGEMM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// The first rungs of the ladder: one output element per lane.
+//
+//  k0  one lane per C element, consecutive lanes walk DOWN a column of C
+//      (amittech.dev, "3.5 Project: tiled matrix multiplication", stage 0):
+//      a wave's A reads and C writes are row-strided - the uncoalesced foil.
+//  k1  consecutive lanes walk ALONG a row of C (same page, stage 1): B reads
+//      and C writes are contiguous per wave and the A element is uniform
+//      across the wave.  On a 64-lane wavefront the workgroup is 64 x 4, so
+//      one wave covers 64 consecutive columns of one row (a 16 x 16 block
+//      would split a wave over four rows and four 64-byte segments).
+//  k2  the same page, stage 2: the workgroup stages a TILE x TILE block of A
+//      and of B in LDS per K step (zero-filled past the matrix edge), with a
+//      barrier after the loads and another before the next overwrite.  Rows
+//      are padded by one float so that lanes reading a column of As fall in
+//      different banks.
+#include "kernels.h"
+
+namespace sgemm {
+
+__global__ void __launch_bounds__(256)
+k0_naive(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+         const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+         int64_t tiles_m, int64_t tiles) {
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t row = (t % tiles_m) * 16 + tx;  // x -> row
+        const int64_t col = (t / tiles_m) * 16 + ty;  // y -> column
+        if (row < M && col < N) {
+            float sum = 0.0f;
+            for (int64_t k = 0; k < K; k++) sum += A[row * lda + k] * B[k * ldb + col];
+            C[row * ldc + col] = sum;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+k1_coalesced(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+             const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+             int64_t tiles_n, int64_t tiles) {
+    const int lane = threadIdx.x % 64;
+    // The row is the same for the whole wave; say so, so that A is read
+    // through the scalar unit once per wave.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t row = (t / tiles_n) * 4 + wave;
+        const int64_t col = (t % tiles_n) * 64 + lane;
+        if (row < M && col < N) {
+            const float* a = A + row * lda;
+            const float* b = B + col;
+            float sum = 0.0f;
+            for (int64_t k = 0; k < K; k++) sum += a[k] * b[k * ldb];
+            C[row * ldc + col] = sum;
+        }
+    }
+}
+
+template <int TILE, int PAD>
+__global__ void __launch_bounds__(TILE * TILE)
+k2_lds(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+       const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+       int64_t tiles_n, int64_t tiles) {
+    __shared__ float As[TILE][TILE + PAD];
+    __shared__ float Bs[TILE][TILE + PAD];
+    const int tx = threadIdx.x % TILE, ty = threadIdx.x / TILE;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t row = (t / tiles_n) * TILE + ty;
+        const int64_t col = (t % tiles_n) * TILE + tx;
+        float sum = 0.0f;
+        for (int64_t k0 = 0; k0 < K; k0 += TILE) {
+            const int64_t ak = k0 + tx, bk = k0 + ty;
+            As[ty][tx] = (row < M && ak < K) ? A[row * lda + ak] : 0.0f;
+            Bs[ty][tx] = (bk < K && col < N) ? B[bk * ldb + col] : 0.0f;
+            __syncthreads();  // the tile is complete before anyone reads it
+#pragma unroll
+            for (int k = 0; k < TILE; k++) sum += As[ty][k] * Bs[k][tx];
+            __syncthreads();  // everyone is done before the next overwrite
+        }
+        if (row < M && col < N) C[row * ldc + col] = sum;
+    }
+}
+
+hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s) {
+    const int64_t tm = ceil_div(g.M, 16), tiles = tm * ceil_div(g.N, 16);
+    hipLaunchKernelGGL(k0_naive, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K, g.A,
+                       g.lda, g.B, g.ldb, g.C, g.ldc, tm, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1_coalesced(const GemmArgs& g, hipStream_t s) {
+    const int64_t tn = ceil_div(g.N, 64), tiles = tn * ceil_div(g.M, 4);
+    hipLaunchKernelGGL(k1_coalesced, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K, g.A,
+                       g.lda, g.B, g.ldb, g.C, g.ldc, tn, tiles);
+    return hipGetLastError();
+}
+
+template <int TILE, int PAD>
+static hipError_t launch_k2_t(const GemmArgs& g, hipStream_t s) {
+    const int64_t tn = ceil_div(g.N, TILE), tiles = tn * ceil_div(g.M, TILE);
+    hipLaunchKernelGGL((k2_lds<TILE, PAD>), dim3(grid_for(tiles)), dim3(TILE * TILE), 0, s, g.M,
+                       g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, tn, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_k2_lds(const GemmArgs& g, int tile, bool padded, hipStream_t s) {
+    if (tile == 16) return padded ? launch_k2_t<16, 1>(g, s) : launch_k2_t<16, 0>(g, s);
+    return padded ? launch_k2_t<32, 1>(g, s) : launch_k2_t<32, 0>(g, s);
+}
+
+}  // namespace sgemm

@@ -1,0 +1,38 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+// Every launcher enqueues on the given stream and returns the launch status;
+// arguments have already been validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace sgemm {
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const float* A;
+    int64_t lda;
+    const float* B;
+    int64_t ldb;
+    float* C;
+    int64_t ldc;
+};
+
+// Upper bound on the number of workgroups a launch uses; kernels loop over
+// tiles beyond it, which keeps grid * block within the 32-bit dispatch size.
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline unsigned grid_for(int64_t tiles) { return unsigned(tiles < kMaxGrid ? tiles : kMaxGrid); }
+
+hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s);
+hipError_t launch_k1_coalesced(const GemmArgs& g, hipStream_t s);
+hipError_t launch_k2_lds(const GemmArgs& g, int tile, bool padded, hipStream_t s);
+hipError_t launch_k3_regtile(const GemmArgs& g, hipStream_t s);
+hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s);
+// Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.
+bool k4_supports(const GemmArgs& g);
+hipError_t launch_zero(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
+hipError_t launch_copy(float* dst, const float* src, int64_t n, int block, int64_t grid, hipStream_t s);
+int64_t copy_default_grid(int64_t n, int block);
+
+}  // namespace sgemm

@@ -1,0 +1,120 @@
+"""The C ABI on the CPU: the library loads, exports what include/sgemm.h
+declares, and rejects bad arguments on the host without any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import roofline_sgemm_f32_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+OK, DIM, LD, NULLPTR, VARIANT, ALIAS, LAUNCH, UNSUPPORTED, ARG = range(9)
+
+# Distinct, non-overlapping fake device addresses: validation never
+# dereferences them and returns before any HIP call.
+PA, PB, PC = 1 << 40, 2 << 40, 3 << 40
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rs.library_path()):
+        pytest.skip("libsgemm.so not built (run __graft_entry__.build())")
+    return rs.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sgemm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(rs.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_and_variant_names(lib):
+    assert rs.status_string(OK) == "ok"
+    for s in range(1, 9):
+        assert rs.status_string(s) not in ("ok", "unknown status")
+    assert rs.status_string(1234) == "unknown status"
+    for name, vid in rs.VARIANTS.items():
+        assert rs.variant_name(vid) == name
+    assert rs.variant_name(99) is None
+    assert lib.sgemm_abi_version() == 1
+
+
+def call(variant, M, N, K, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return rs.sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, None)
+
+
+@pytest.mark.parametrize("variant", list(rs.VARIANTS.values()))
+def test_validation_codes(lib, variant):
+    assert call(variant, -1, 4, 4) == DIM
+    assert call(variant, 4, -1, 4) == DIM
+    assert call(variant, 4, 4, -1) == DIM
+    assert call(variant, 4, 4, 8, lda=7) == LD
+    assert call(variant, 4, 8, 4, ldb=7) == LD
+    assert call(variant, 4, 8, 4, ldc=7) == LD
+    assert call(variant, 4, 4, 0, lda=0) == LD  # lda >= max(1, K)
+    assert call(variant, 4, 4, 4, C=None) == NULLPTR
+    assert call(variant, 4, 4, 4, A=None) == NULLPTR
+    assert call(variant, 4, 4, 4, B=None) == NULLPTR
+    # Empty outputs are a successful no-op even with null pointers.
+    assert call(variant, 0, 4, 4, A=None, B=None, C=None) == OK
+    assert call(variant, 4, 0, 4, A=None, B=None, C=None) == OK
+    # Output overlapping an input.
+    assert call(variant, 4, 4, 4, C=PA + 4) == ALIAS
+    assert call(variant, 4, 4, 4, C=PB - 8) == ALIAS
+
+
+def test_unknown_variant(lib):
+    assert call(8, 4, 4, 4) == VARIANT
+    assert call(-1, 4, 4, 4) == VARIANT
+
+
+def test_alias_edges(lib):
+    # C's last element is A's first element: overlap by one float.
+    M, N, K = 3, 5, 7
+    c_bytes = ((M - 1) * N + N) * 4
+    assert call(4, M, N, K, C=PA - c_bytes + 4, A=PA) == ALIAS
+    # A's last element is C's first.
+    a_bytes = ((M - 1) * K + K) * 4
+    assert call(4, M, N, K, C=PA + a_bytes - 4, A=PA) == ALIAS
+
+
+def test_k4_rejects_offsets_beyond_32_bits_and_auto_falls_back(lib):
+    M, N, K, lda = 256, 256, 16, 1 << 25  # 127 rows of lda exceed 2 GiB of offset
+    assert call(4, M, N, K, lda=lda) == UNSUPPORTED
+    auto = lib.sgemm_auto_variant(M, N, K, PA, lda, PB, N, PC, N)
+    assert auto == rs.VARIANTS["k3_regtile_db"]
+    assert lib.sgemm_auto_variant(4096, 4096, 4096, PA, 4096, PB, 4096, PC, 4096) == rs.VARIANTS["k4_mfma"]
+    assert lib.sgemm_auto_variant(-1, 4, 4, PA, 4, PB, 4, PC, 4) == -DIM
+
+
+def test_copy_validation(lib):
+    f = lib.sgemm_copy_f32_launch
+    assert f(PB, PA, -1, 256, 16, None) == ARG
+    assert f(PB, PA, 100, 100, 16, None) == ARG
+    assert f(PB, PA, 100, 2048, 16, None) == ARG
+    assert f(PB, PA, 100, 256, 0, None) == ARG
+    assert f(PB, PA, 0, 256, 16, None) == OK
+    assert f(None, PA, 100, 256, 16, None) == NULLPTR
+    assert f(PA + 8, PA, 100, 256, 16, None) == ALIAS
+    assert lib.sgemm_copy_f32(PA, PA, -5, None) == ARG
+    assert lib.sgemm_copy_f32(PA, PA, 0, None) == OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        rs.sgemm(torch.ones(2, 2), torch.ones(2, 2))

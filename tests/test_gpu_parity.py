@@ -1,0 +1,237 @@
+"""GPU parity: every ladder variant against the CPU oracle, through the C ABI.
+
+Bar: every element within |C - C_ref| <= 4 K 2^-24 sum_k |a_ik b_kj| of the
+double-precision oracle (the checker in oracle.check), every element written
+(C is prefilled with NaN), C's padding and the memory after it untouched.
+Integer-valued inputs make every partial sum exact in float, so there the
+GPU must equal the oracle bit for bit in any summation order.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check
+from roofline_sgemm_f32_amd.inputs import WORKLOADS, as_numpy, make_operands, workload_operands
+import roofline_sgemm_f32_amd as rs
+from tests.gpu_util import run, to_device
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16", "k2_lds_tiled32_nopad",
+       "k3_regtile_db", "k4_mfma", "auto"]
+FAST = ["k3_regtile_db", "k4_mfma", "auto"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rs.load()
+    oracle.load()
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def full_check(variant, M, N, K, dist="uniform", seed=0, lda=None, ldb=None, ldc=None):
+    A, B = make_operands(M, N, K, dist, seed, lda=lda, ldb=ldb)
+    C, out = run(variant, A, B, ldc=ldc)
+    ref, S = oracle.sgemm_f64(as_numpy(A), as_numpy(B))
+    rep = check.check(C, ref, S, K)
+    assert out.guard_intact(), f"{variant} {M}x{N}x{K}: wrote outside C"
+    assert rep["ok"], f"{variant} {M}x{N}x{K}: {rep}"
+    if dist == "int":
+        assert np.array_equal(C.astype(np.float64), ref), f"{variant} {M}x{N}x{K}: not exact"
+    return C, rep
+
+
+SHAPES = [
+    (1, 1, 1), (7, 5, 3), (33, 65, 17), (64, 64, 64), (127, 129, 31), (128, 128, 16),
+    (129, 257, 33), (200, 300, 1), (256, 256, 256), (96, 160, 1000), (300, 17, 129),
+]
+
+
+@pytest.mark.parametrize("variant", ALL)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes_uniform(variant, shape):
+    M, N, K = shape
+    note(f"[parity] {variant} {M}x{N}x{K}")
+    full_check(variant, M, N, K, "uniform", seed=M + 3 * N + 7 * K)
+
+
+@pytest.mark.parametrize("variant", ALL)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes_integer_exact(variant, shape):
+    M, N, K = shape
+    note(f"[exact] {variant} {M}x{N}x{K}")
+    full_check(variant, M, N, K, "int", seed=11 * M + N + K)
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_padded_leading_dimensions(variant):
+    # lda > K, ldb > N, ldc > N; odd values break 16-byte row alignment.
+    for (M, N, K, lda, ldb, ldc) in [(70, 90, 50, 53, 97, 91), (130, 132, 40, 44, 136, 140),
+                                     (65, 129, 257, 261, 131, 133)]:
+        note(f"[ld] {variant} {M}x{N}x{K} lda={lda} ldb={ldb} ldc={ldc}")
+        full_check(variant, M, N, K, "int", seed=5, lda=lda, ldb=ldb, ldc=ldc)
+        full_check(variant, M, N, K, "uniform", seed=6, lda=lda, ldb=ldb, ldc=ldc)
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_k_zero_writes_zeros(variant):
+    note(f"[k0] {variant}")
+    A = torch.zeros((37, 0))
+    B = torch.zeros((0, 41))
+    C, out = run(variant, A, B, ldc=45)
+    assert np.all(C == 0.0) and out.guard_intact()
+
+
+@pytest.mark.parametrize("variant", ALL)
+def test_empty_output_is_noop(variant):
+    assert rs.sgemm_f32_variant(variant, 0, 5, 5, 0, 5, 0, 5, 0, 5, None) == 0
+    assert rs.sgemm_f32_variant(variant, 5, 0, 5, 0, 5, 0, 1, 0, 1, None) == 0
+
+
+@pytest.mark.parametrize("variant", FAST)
+def test_edge_sweep_1_to_9(variant):
+    # Every (M, N, K) in 1..9: exact integer inputs, bitwise.
+    note(f"[sweep9] {variant}")
+    for M in range(1, 10):
+        for N in range(1, 10):
+            for K in range(1, 10):
+                full_check(variant, M, N, K, "int", seed=M * 100 + N * 10 + K)
+
+
+@pytest.mark.parametrize("variant", ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16",
+                                     "k2_lds_tiled32_nopad"])
+def test_edge_sweep_1_to_5(variant):
+    note(f"[sweep5] {variant}")
+    for M in range(1, 6):
+        for N in range(1, 6):
+            for K in range(1, 6):
+                full_check(variant, M, N, K, "int", seed=M * 100 + N * 10 + K)
+
+
+@pytest.mark.parametrize("variant", FAST)
+def test_tile_boundaries(variant):
+    for n in (31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257):
+        note(f"[tile] {variant} n={n}")
+        full_check(variant, n, n, n, "int", seed=n)
+        full_check(variant, n, 2 * n + 1, (n // 2) + 3, "uniform", seed=n + 1)
+
+
+@pytest.mark.parametrize("variant", FAST)
+def test_unaligned_pointers(variant):
+    # Operands starting 4 bytes past a 16-byte boundary take the 4-byte load path.
+    M, N, K = 100, 132, 68
+    A, B = make_operands(M, N, K, "int", seed=9)
+    Ad = torch.empty(M * K + 1, device="cuda")[1:].view(M, K)
+    Ad.copy_(A.cuda())
+    Bd = torch.empty(K * N + 1, device="cuda")[1:].view(K, N)
+    Bd.copy_(B.cuda())
+    note(f"[unaligned] {variant}")
+    C, out = run(variant, A, B, A_dev=Ad, B_dev=Bd)
+    ref, S = oracle.sgemm_f64(as_numpy(A), as_numpy(B))
+    assert np.array_equal(C.astype(np.float64), ref) and out.guard_intact()
+
+
+# --- invariants ----------------------------------------------------------
+
+@pytest.mark.parametrize("variant", FAST)
+def test_identity_and_scaling(variant):
+    M, N, K = 200, 150, 130
+    A, B = make_operands(M, N, K, "uniform", seed=21)
+    note(f"[identity] {variant}")
+    C_ai, _ = run(variant, A, torch.eye(K))
+    assert np.array_equal(C_ai, as_numpy(A)), "A * I != A"
+    Bk = make_operands(K, N, K, "uniform", 22)[1]
+    C_ib, _ = run(variant, torch.eye(K), Bk)
+    assert np.array_equal(C_ib, as_numpy(Bk)), "I * B != B"
+    C1, _ = run(variant, A, B)
+    C2, _ = run(variant, A * 2, B)
+    assert np.array_equal(C2, 2 * C1), "(2A) B != 2 (A B)"
+    C3, _ = run(variant, A, B)
+    assert np.array_equal(C1, C3), "run-to-run difference"
+
+
+@pytest.mark.parametrize("variant", FAST)
+def test_all_ones_gives_row_sums(variant):
+    M, N, K = 77, 300, 513
+    A, _ = make_operands(M, N, K, "uniform", seed=31)
+    note(f"[ones] {variant}")
+    C, _ = run(variant, A, torch.ones((K, N)))
+    Ad = as_numpy(A).astype(np.float64)
+    rowsum, S = Ad.sum(axis=1), np.abs(Ad).sum(axis=1)
+    rep = check.check(C, np.repeat(rowsum[:, None], N, 1), np.repeat(S[:, None], N, 1), K)
+    assert rep["ok"], rep
+    # Every column sees the same k order, so a row is constant.
+    assert np.all(C == C[:, :1])
+
+
+def test_row_permutation_k4():
+    M, N, K = 256, 256, 300
+    A, B = make_operands(M, N, K, "normal", seed=41)
+    perm = torch.randperm(M, generator=torch.Generator().manual_seed(1))
+    C, _ = run("k4_mfma", A, B)
+    Cp, _ = run("k4_mfma", A[perm].contiguous(), B)
+    assert np.array_equal(Cp, C[perm.numpy()])
+
+
+# --- the five workloads ---------------------------------------------------
+
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(n, size=min(k, n), replace=False).tolist())
+    pick.update({0, n - 1, min(n - 1, 127), min(n - 1, 128)})
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.parametrize("variant", ["auto", "k4_mfma"])
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload(variant, name):
+    """The workloads at full size: complete check where the oracle is quick
+    (square256, square1024), else sampled rows and columns (every tile row
+    and column position is hit by some sample), plus all-finite."""
+    w = WORKLOADS[name]
+    note(f"[workload] {variant} {name}")
+    A, B = workload_operands(w)
+    C, out = run(variant, A, B, ldc=w.ldc)
+    assert np.isfinite(C).all(), "unwritten or non-finite output"
+    An, Bn = as_numpy(A), as_numpy(B)
+    if w.M * w.N * w.K <= 1024 ** 3:
+        ref, S = oracle.sgemm_f64(An, Bn)
+        rep = check.check(C, ref, S, w.K)
+        assert rep["ok"], rep
+    else:
+        rows = _sample(w.M, 24, 1)
+        ref, S = oracle.sgemm_rows_f64(An, Bn, rows)
+        rep = check.check(C[rows], ref, S, w.K)
+        assert rep["ok"], ("rows", rep)
+        cols = _sample(w.N, 24, 2)
+        ref, S = oracle.sgemm_f64(An, np.ascontiguousarray(Bn[:, cols]))
+        rep = check.check(C[:, cols], ref, S, w.K)
+        assert rep["ok"], ("cols", rep)
+    note(f"[workload] {variant} {name}: max bound use {rep['max_bound_util']:.3g}, "
+         f"page rel err {rep['max_rel_err_page']:.3g}")
+
+
+@pytest.mark.parametrize("name", ["square4096", "ragged3001x4099x2047"])
+def test_workload_integer_exact(name):
+    """Full-size shapes with integer inputs: sampled rows and columns must be
+    bit-identical to the oracle."""
+    w = WORKLOADS[name]
+    note(f"[workload-int] {name}")
+    A, B = make_operands(w.M, w.N, w.K, "int", seed=w.seed, lda=w.lda, ldb=w.ldb)
+    C, out = run("auto", A, B, ldc=w.ldc)
+    An, Bn = as_numpy(A), as_numpy(B)
+    rows = _sample(w.M, 16, 3)
+    ref, _ = oracle.sgemm_rows_f64(An, Bn, rows, bound=False)
+    assert np.array_equal(C[rows].astype(np.float64), ref)
+    cols = _sample(w.N, 16, 4)
+    ref, _ = oracle.sgemm_f64(An, np.ascontiguousarray(Bn[:, cols]), bound=False)
+    assert np.array_equal(C[:, cols].astype(np.float64), ref)
