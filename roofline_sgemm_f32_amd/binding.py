@@ -21,8 +21,9 @@ VARIANTS = {
     "k3_regtile_db": 3,
     "k4_mfma": 4,
     "k2_lds_tiled16": 5,
-    "k2_lds_tiled32_nopad": 6,
+    "k2_lds_tiled32_pad1": 6,
     "k0_naive": 7,
+    "k2_lds_tiled16_pad1": 8,
 }
 
 # sgemm_status_t

@@ -72,9 +72,10 @@ int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float*
     switch (variant) {
         case SGEMM_K0_NAIVE: return launch_status(sgemm::launch_k0_naive(g, s));
         case SGEMM_K1_COALESCED: return launch_status(sgemm::launch_k1_coalesced(g, s));
-        case SGEMM_K2_LDS_TILED: return launch_status(sgemm::launch_k2_lds(g, 32, true, s));
-        case SGEMM_K2_LDS_TILED16: return launch_status(sgemm::launch_k2_lds(g, 16, true, s));
-        case SGEMM_K2_LDS_TILED_NOPAD: return launch_status(sgemm::launch_k2_lds(g, 32, false, s));
+        case SGEMM_K2_LDS_TILED: return launch_status(sgemm::launch_k2_lds(g, 32, 0, s));
+        case SGEMM_K2_LDS_TILED16: return launch_status(sgemm::launch_k2_lds(g, 16, 0, s));
+        case SGEMM_K2_LDS_TILED_PAD1: return launch_status(sgemm::launch_k2_lds(g, 32, 1, s));
+        case SGEMM_K2_LDS_TILED16_PAD1: return launch_status(sgemm::launch_k2_lds(g, 16, 1, s));
         case SGEMM_K3_REGTILE_DB: return launch_status(sgemm::launch_k3_regtile(g, s));
         case SGEMM_K4_MFMA:
             if (!sgemm::k4_supports(g)) return SGEMM_ERR_UNSUPPORTED;
@@ -135,10 +136,11 @@ const char* sgemm_variant_name(int variant) {
         case SGEMM_AUTO: return "auto";
         case SGEMM_K1_COALESCED: return "k1_coalesced";
         case SGEMM_K2_LDS_TILED: return "k2_lds_tiled32";
+        case SGEMM_K2_LDS_TILED16_PAD1: return "k2_lds_tiled16_pad1";
         case SGEMM_K3_REGTILE_DB: return "k3_regtile_db";
         case SGEMM_K4_MFMA: return "k4_mfma";
         case SGEMM_K2_LDS_TILED16: return "k2_lds_tiled16";
-        case SGEMM_K2_LDS_TILED_NOPAD: return "k2_lds_tiled32_nopad";
+        case SGEMM_K2_LDS_TILED_PAD1: return "k2_lds_tiled32_pad1";
         case SGEMM_K0_NAIVE: return "k0_naive";
         default: return nullptr;
     }

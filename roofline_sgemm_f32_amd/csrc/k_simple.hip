@@ -10,9 +10,19 @@
 //      would split a wave over four rows and four 64-byte segments).
 //  k2  the same page, stage 2: the workgroup stages a TILE x TILE block of A
 //      and of B in LDS per K step (zero-filled past the matrix edge), with a
-//      barrier after the loads and another before the next overwrite.  Rows
-//      are padded by one float so that lanes reading a column of As fall in
-//      different banks.
+//      barrier after the loads and another before the next overwrite.
+//
+//      LDS banking on gfx950: 64 banks of 4 bytes, and a wave's 64 lanes are
+//      served together.  A wave of the 32 x 32 workgroup covers two tile rows
+//      (lanes 0-31 row ty, lanes 32-63 row ty+1); with a row stride of 32
+//      floats the two halves fall in banks b..b+31 and b+32..b+63, so the
+//      unpadded tile is already conflict-free, and its 128-byte aligned rows
+//      let the inner loop read A four floats at a time.  A wave of the
+//      16 x 16 workgroup covers four rows at stride 16: banks 16r..16r+15,
+//      again all 64 distinct.  Padding rows by one float (stride 33 or 17)
+//      is the comparison point: it stays conflict-free at 32 but loses the
+//      vector reads, and at 16 the fourth row wraps onto the first row's
+//      banks.
 #include "kernels.h"
 
 namespace sgemm {
@@ -101,9 +111,9 @@ static hipError_t launch_k2_t(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_k2_lds(const GemmArgs& g, int tile, bool padded, hipStream_t s) {
-    if (tile == 16) return padded ? launch_k2_t<16, 1>(g, s) : launch_k2_t<16, 0>(g, s);
-    return padded ? launch_k2_t<32, 1>(g, s) : launch_k2_t<32, 0>(g, s);
+hipError_t launch_k2_lds(const GemmArgs& g, int tile, int pad, hipStream_t s) {
+    if (tile == 16) return pad ? launch_k2_t<16, 1>(g, s) : launch_k2_t<16, 0>(g, s);
+    return pad ? launch_k2_t<32, 1>(g, s) : launch_k2_t<32, 0>(g, s);
 }
 
 }  // namespace sgemm

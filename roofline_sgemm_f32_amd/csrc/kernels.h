@@ -26,7 +26,7 @@ inline unsigned grid_for(int64_t tiles) { return unsigned(tiles < kMaxGrid ? til
 
 hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k1_coalesced(const GemmArgs& g, hipStream_t s);
-hipError_t launch_k2_lds(const GemmArgs& g, int tile, bool padded, hipStream_t s);
+hipError_t launch_k2_lds(const GemmArgs& g, int tile, int pad, hipStream_t s);
 hipError_t launch_k3_regtile(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.

@@ -20,7 +20,7 @@ from tests.gpu_util import run, to_device
 
 pytestmark = pytest.mark.gpu
 
-ALL = ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16", "k2_lds_tiled32_nopad",
+ALL = ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16", "k2_lds_tiled32_pad1", "k2_lds_tiled16_pad1",
        "k3_regtile_db", "k4_mfma", "auto"]
 FAST = ["k3_regtile_db", "k4_mfma", "auto"]
 
@@ -108,7 +108,7 @@ def test_edge_sweep_1_to_9(variant):
 
 
 @pytest.mark.parametrize("variant", ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16",
-                                     "k2_lds_tiled32_nopad"])
+                                     "k2_lds_tiled32_pad1", "k2_lds_tiled16_pad1"])
 def test_edge_sweep_1_to_5(variant):
     note(f"[sweep5] {variant}")
     for M in range(1, 6):
