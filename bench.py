@@ -199,7 +199,27 @@ def copy_probe(steps: int, block=None, grid=None):
     gbs = m.gbs(m.copy_bytes(n), per)
     return {"n": n, "bytes": m.copy_bytes(n), "ms": round(per, 5), "gbs": round(gbs, 1),
             "frac": round(gbs / m.MI355X_HBM_GBS, 4), "exact": ok,
-            "block": block or 256, "grid": grid}
+            "block": block or 64, "grid": grid}
+
+
+def compute_probe(valu_iters=4096, mfma_iters=2048):
+    """Sustained FP32 rate of register-only multiply-add chains (vector ALU)
+    and of back-to-back FP32 matrix instructions, for the compute roof."""
+    import torch
+    import roofline_sgemm_f32_amd as rs
+    from roofline_sgemm_f32_amd.inputs import probe_operands
+    blocks, block = 256 * 8, 256  # 32 waves per CU
+    out_v = torch.empty((blocks * block, 16), device="cuda")
+    _, per_v = time_launches(lambda: rs.probe_valu(blocks, block, valu_iters, 0.999, 0.001, out_v), 5, 1)
+    valu_tf = blocks * block * valu_iters * 16 * 2 / (per_v * 1e-3) / 1e12
+    a, b = probe_operands(7)
+    a, b = a.cuda(), b.cuda()
+    mblocks = 256 * 4  # 16 waves per CU
+    out_m = torch.empty((mblocks * 4, 4, 32, 32), device="cuda")
+    _, per_m = time_launches(lambda: rs.probe_mfma(a, b, mblocks, mfma_iters, out_m), 5, 1)
+    mfma_tf = mblocks * 16 * mfma_iters * 4096 / (per_m * 1e-3) / 1e12
+    return {"valu_fma_tflops": round(valu_tf, 2), "mfma_f32_tflops": round(mfma_tf, 2),
+            "valu_ms": round(per_v, 4), "mfma_ms": round(per_m, 4)}
 
 
 def ladder(args, out):
@@ -255,6 +275,8 @@ def main():
                    help="target duration of the CPU oracle sample (0 skips the leg)")
     p.add_argument("--copy-steps", type=int, default=50)
     p.add_argument("--copy-sweep", action="store_true", help="block x grid sweep of the copy probe")
+    p.add_argument("--no-compute-probe", dest="compute_probe", action="store_false",
+                   help="skip the register-only FMA / MFMA rate probe")
     p.add_argument("--ladder", action="store_true", help="time every variant (table on stderr)")
     p.add_argument("--ladder-workloads", default="square4096")
     p.add_argument("--ladder-reps", type=int, default=20)
@@ -304,6 +326,10 @@ def main():
     copy = copy_probe(args.copy_steps) if args.copy_steps > 0 else None
     if copy:
         log(f"[bench] copy probe {copy['gbs']} GB/s ({100 * copy['frac']:.1f}% of 8 TB/s)")
+    probe = compute_probe() if args.compute_probe else None
+    if probe:
+        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s, "
+            f"FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s")
     if args.copy_sweep:
         from roofline_sgemm_f32_amd.inputs import COPY_ELEMENTS  # noqa: F401
         for block in (64, 128, 256, 512, 1024):
@@ -341,6 +367,7 @@ def main():
         "cpu_baseline": cpu,
         "gate": gate,
         "hbm_copy": copy,
+        "compute_probe": probe,
     }
     if out:
         out.write(json.dumps({"bench": line}) + "\n")

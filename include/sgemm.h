@@ -96,9 +96,35 @@ int sgemm_copy_f32(float *dst, const float *src, int64_t n, void *stream);
 
 /* The same copy with an explicit launch shape, for the exercise's block and
  * grid sweep: block is the workgroup size (a multiple of 64, 64..1024), grid
- * the number of workgroups (1..2^20).  Invalid values give SGEMM_ERR_ARG. */
+ * the number of workgroups (1..2^22).  Invalid values give SGEMM_ERR_ARG. */
 int sgemm_copy_f32_launch(float *dst, const float *src, int64_t n,
                           int block, int64_t grid, void *stream);
+
+/* Compute-roof probes (amittech.dev, "7.3 Bandwidths and peak rate -
+ * exercises", exercise 5: register-only multiply-add chains that measure the
+ * sustained arithmetic rate).
+ *
+ * sgemm_probe_valu_f32: blocks x block lanes (block a multiple of 64 in
+ * 64..1024, blocks in 1..2^20); lane t runs 16 independent chains, chain j
+ * starting at (j + 1) / 16 and updated iters times as acc = fmaf(acc, x, y),
+ * and writes the 16 final values to out[16 t .. 16 t + 15].  out is a device
+ * buffer of blocks * block * 16 floats owned by the caller.  Work:
+ * blocks * block * iters * 16 * 2 FLOP.
+ *
+ * sgemm_probe_mfma_f32: blocks workgroups of 4 waves (1..2^20).  Every wave
+ * accumulates iters products A * B (A 32 x 2 with A[i][k] = a_vals[i + 32 k],
+ * B 2 x 32 with B[k][j] = b_vals[j + 32 k]; a_vals and b_vals are device
+ * arrays of 64 floats) into 4 independent 32 x 32 float accumulators with the
+ * FP32 matrix instruction, and writes accumulator q of wave w row-major to
+ * out[(4 w + q) * 1024 ...].  out holds blocks * 16 * 1024 floats.  Work:
+ * blocks * 16 * iters * 4096 FLOP.
+ *
+ * Both validate their arguments (SGEMM_ERR_ARG, SGEMM_ERR_NULLPTR) before
+ * any HIP call and enqueue on stream without synchronising. */
+int sgemm_probe_valu_f32(float *out, int64_t blocks, int block, int64_t iters,
+                         float x, float y, void *stream);
+int sgemm_probe_mfma_f32(float *out, const float *a_vals, const float *b_vals,
+                         int64_t blocks, int64_t iters, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *sgemm_status_string(int status);

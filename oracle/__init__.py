@@ -65,6 +65,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_sgemm_rows_f64.restype = cint
     lib.oracle_sgemm_entries_f64.argtypes = [i64, vp, vp, i64, vp, i64, vp, i64, vp, vp]
     lib.oracle_sgemm_entries_f64.restype = cint
+    lib.oracle_fma_chain_f32.argtypes = [i64, ctypes.c_float, ctypes.c_float, cint, vp]
+    lib.oracle_fma_chain_f32.restype = None
+    lib.oracle_mfma_probe_f64.argtypes = [i64, vp, vp, vp]
+    lib.oracle_mfma_probe_f64.restype = None
     return lib
 
 
@@ -155,3 +159,23 @@ def sgemm_entries_f64(A: np.ndarray, B: np.ndarray, rows, cols, lib: ctypes.CDLL
     if rc != 0:
         raise RuntimeError("oracle_sgemm_entries_f64 failed")
     return out, S
+
+
+def fma_chain_f32(iters: int, x: float, y: float, chains: int = 16, lib: ctypes.CDLL | None = None):
+    """Final values of the compute probe's multiply-add chains (float32)."""
+    lib = lib or load()
+    out = np.empty(chains, dtype=np.float32)
+    lib.oracle_fma_chain_f32(iters, x, y, chains, _ptr(out))
+    return out
+
+
+def mfma_probe_f64(iters: int, a_vals: np.ndarray, b_vals: np.ndarray, lib: ctypes.CDLL | None = None):
+    """The 32 x 32 matrix the matrix-unit probe accumulates, in double."""
+    lib = lib or load()
+    a = np.ascontiguousarray(a_vals, dtype=np.float32)
+    b = np.ascontiguousarray(b_vals, dtype=np.float32)
+    if a.size != 64 or b.size != 64:
+        raise ValueError("a_vals and b_vals hold 64 values each")
+    D = np.empty((32, 32), dtype=np.float64)
+    lib.oracle_mfma_probe_f64(iters, _ptr(a), _ptr(b), _ptr(D))
+    return D

@@ -136,3 +136,32 @@ int oracle_sgemm_entries_f64(int64_t count, const int64_t *rows, const int64_t *
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Compute-roof probes (amittech.dev, "7.3 Bandwidths and peak rate -
+ * exercises", exercise 5).
+ *
+ * Chain probe: chain j (0 <= j < chains) starts at (j + 1) / 16 and is
+ * updated iters times as acc = acc * x + y with a single rounding (fmaf),
+ * which is what a fused multiply-add instruction computes.
+ */
+void oracle_fma_chain_f32(int64_t iters, float x, float y, int chains, float *out) {
+    for (int j = 0; j < chains; j++) {
+        float acc = 0.0625f * (float)(j + 1);
+        for (int64_t i = 0; i < iters; i++) acc = fmaf(acc, x, y);
+        out[j] = acc;
+    }
+}
+
+/* Matrix-unit probe: the 32 x 32 result of adding the product of A (32 x 2,
+ * A[i][k] = a_vals[i + 32 k]) and B (2 x 32, B[k][j] = b_vals[j + 32 k])
+ * iters times, in double, row-major.  With small integer operands every
+ * partial sum is exact in float too. */
+void oracle_mfma_probe_f64(int64_t iters, const float *a_vals, const float *b_vals, double *D) {
+    for (int i = 0; i < 32; i++)
+        for (int j = 0; j < 32; j++) {
+            double p = 0.0;
+            for (int k = 0; k < 2; k++) p += (double)a_vals[i + 32 * k] * (double)b_vals[j + 32 * k];
+            D[i * 32 + j] = (double)iters * p;
+        }
+}

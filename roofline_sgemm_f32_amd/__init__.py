@@ -6,9 +6,9 @@ ctypes layer over it.  Importing the package does not load the library; the
 first call does, and raises if it is missing.
 """
 from .binding import (EXPORTS, STATUS, VARIANTS, SgemmError, copy_f32, copy_f32_launch,
-                      library_path, load, sgemm, sgemm_f32, sgemm_f32_variant, status_string,
-                      variant_name)
+                      library_path, load, probe_mfma, probe_valu, sgemm, sgemm_f32,
+                      sgemm_f32_variant, status_string, variant_name)
 
 __all__ = ["EXPORTS", "STATUS", "VARIANTS", "SgemmError", "copy_f32", "copy_f32_launch",
-           "library_path", "load", "sgemm", "sgemm_f32", "sgemm_f32_variant", "status_string",
+           "library_path", "load", "probe_mfma", "probe_valu", "sgemm", "sgemm_f32", "sgemm_f32_variant", "status_string",
            "variant_name"]

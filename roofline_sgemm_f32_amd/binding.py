@@ -35,7 +35,8 @@ STATUS = {
 
 EXPORTS = ["sgemm_f32", "sgemm_f32_variant", "sgemm_copy_f32", "sgemm_copy_f32_launch",
            "sgemm_status_string", "sgemm_variant_name", "sgemm_auto_variant",
-           "sgemm_last_hip_error", "sgemm_abi_version"]
+           "sgemm_last_hip_error", "sgemm_abi_version", "sgemm_probe_valu_f32",
+           "sgemm_probe_mfma_f32"]
 
 
 class SgemmError(RuntimeError):
@@ -76,6 +77,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_auto_variant.restype = cint
     lib.sgemm_last_hip_error.argtypes = []
     lib.sgemm_last_hip_error.restype = cint
+    lib.sgemm_probe_valu_f32.argtypes = [vp, i64, cint, i64, ctypes.c_float, ctypes.c_float, vp]
+    lib.sgemm_probe_valu_f32.restype = cint
+    lib.sgemm_probe_mfma_f32.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.sgemm_probe_mfma_f32.restype = cint
     lib.sgemm_abi_version.argtypes = []
     lib.sgemm_abi_version.restype = cint
     if path is None:
@@ -169,3 +174,43 @@ def copy_f32_launch(dst, src, block: int, grid: int):
     if st != 0:
         raise SgemmError(st, "sgemm_copy_f32_launch")
     return dst
+
+
+VALU_CHAINS = 16
+MFMA_WAVES_PER_BLOCK = 4
+MFMA_ACC_PER_WAVE = 4
+
+
+def probe_valu(blocks: int, block: int, iters: int, x: float, y: float, out=None):
+    """Run the VALU multiply-add probe; returns the (blocks*block, 16) output
+    tensor (final chain values).  Work: blocks*block*iters*16*2 FLOP."""
+    import torch
+    if out is None:
+        out = torch.empty((blocks * block, VALU_CHAINS), dtype=torch.float32, device="cuda")
+    elif out.numel() < blocks * block * VALU_CHAINS or not out.is_contiguous():
+        raise ValueError("out too small or not contiguous")
+    st = load().sgemm_probe_valu_f32(out.data_ptr(), blocks, block, iters, x, y,
+                                     _stream_handle(out.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_probe_valu_f32")
+    return out
+
+
+def probe_mfma(a_vals, b_vals, blocks: int, iters: int, out=None):
+    """Run the matrix-core probe; returns (blocks*4, 4, 32, 32) accumulators.
+    Work: blocks*16*iters*4096 FLOP."""
+    import torch
+    n = blocks * MFMA_WAVES_PER_BLOCK * MFMA_ACC_PER_WAVE
+    if out is None:
+        out = torch.empty((blocks * MFMA_WAVES_PER_BLOCK, MFMA_ACC_PER_WAVE, 32, 32),
+                          dtype=torch.float32, device="cuda")
+    elif out.numel() < n * 1024 or not out.is_contiguous():
+        raise ValueError("out too small or not contiguous")
+    for v in (a_vals, b_vals):
+        if v.numel() != 64 or v.dtype != torch.float32 or v.device.type != "cuda" or not v.is_contiguous():
+            raise ValueError("a_vals and b_vals must be 64 contiguous float32 GPU values")
+    st = load().sgemm_probe_mfma_f32(out.data_ptr(), a_vals.data_ptr(), b_vals.data_ptr(), blocks,
+                                     iters, _stream_handle(out.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_probe_mfma_f32")
+    return out

@@ -101,7 +101,7 @@ int sgemm_copy_f32_launch(float* dst, const float* src, int64_t n, int block, in
                           void* stream) {
     if (n < 0) return SGEMM_ERR_ARG;
     if (block < 64 || block > 1024 || block % 64 != 0) return SGEMM_ERR_ARG;
-    if (grid < 1 || grid > sgemm::kMaxGrid) return SGEMM_ERR_ARG;
+    if (grid < 1 || grid > sgemm::kMaxCopyGrid) return SGEMM_ERR_ARG;
     if (n == 0) return SGEMM_OK;
     if (dst == nullptr || src == nullptr) return SGEMM_ERR_NULLPTR;
     const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
@@ -112,8 +112,27 @@ int sgemm_copy_f32_launch(float* dst, const float* src, int64_t n, int block, in
 }
 
 int sgemm_copy_f32(float* dst, const float* src, int64_t n, void* stream) {
-    const int block = 256;
+    const int block = sgemm::kCopyBlock;
     return sgemm_copy_f32_launch(dst, src, n, block, sgemm::copy_default_grid(n, block), stream);
+}
+
+int sgemm_probe_valu_f32(float* out, int64_t blocks, int block, int64_t iters, float x, float y,
+                         void* stream) {
+    if (blocks < 1 || blocks > sgemm::kMaxGrid) return SGEMM_ERR_ARG;
+    if (block < 64 || block > 1024 || block % 64 != 0) return SGEMM_ERR_ARG;
+    if (iters < 0) return SGEMM_ERR_ARG;
+    if (out == nullptr) return SGEMM_ERR_NULLPTR;
+    return launch_status(sgemm::launch_probe_valu(out, iters, x, y, blocks, block,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int sgemm_probe_mfma_f32(float* out, const float* a_vals, const float* b_vals, int64_t blocks,
+                         int64_t iters, void* stream) {
+    if (blocks < 1 || blocks > sgemm::kMaxGrid) return SGEMM_ERR_ARG;
+    if (iters < 0) return SGEMM_ERR_ARG;
+    if (out == nullptr || a_vals == nullptr || b_vals == nullptr) return SGEMM_ERR_NULLPTR;
+    return launch_status(sgemm::launch_probe_mfma(out, a_vals, b_vals, iters, blocks,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 const char* sgemm_status_string(int status) {

@@ -21,6 +21,11 @@ struct GemmArgs {
 // tiles beyond it, which keeps grid * block within the 32-bit dispatch size.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
+// Copy probe: workgroup count limit (grid * block stays below 2^32 work-items
+// for blocks of up to 1024 lanes).
+constexpr int64_t kMaxCopyGrid = int64_t(1) << 22;
+constexpr int kCopyBlock = 64;
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline unsigned grid_for(int64_t tiles) { return unsigned(tiles < kMaxGrid ? tiles : kMaxGrid); }
 
@@ -34,5 +39,9 @@ bool k4_supports(const GemmArgs& g);
 hipError_t launch_zero(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, int block, int64_t grid, hipStream_t s);
 int64_t copy_default_grid(int64_t n, int block);
+hipError_t launch_probe_valu(float* out, int64_t iters, float x, float y, int64_t blocks, int block,
+                             hipStream_t s);
+hipError_t launch_probe_mfma(float* out, const float* a_vals, const float* b_vals, int64_t iters,
+                             int64_t blocks, hipStream_t s);
 
 }  // namespace sgemm

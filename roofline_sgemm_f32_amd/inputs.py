@@ -99,3 +99,11 @@ def copy_source(n: int = COPY_ELEMENTS, seed: int = COPY_SEED) -> torch.Tensor:
 def as_numpy(x: torch.Tensor) -> np.ndarray:
     """A numpy view of a CPU float32 tensor that keeps its strides."""
     return x.numpy()
+
+
+def probe_operands(seed: int = 7, dist: str = "int"):
+    """Operand values of the matrix-unit probe: 64 for A, then 64 for B."""
+    g = torch.Generator().manual_seed(seed)
+    a = _draw(g, 1, 64, dist).reshape(64)
+    b = _draw(g, 1, 64, dist).reshape(64)
+    return a, b

@@ -11,7 +11,10 @@ raises AssertionError when the oracle disagrees with:
 * closed forms: A * I = A and I * B = B exactly; B = ones gives row sums of A;
 * a library routine on a case that reduces to it: integer inputs make the
   product exact, equal to numpy's int64 matrix product;
-* degenerate sizes: K = 0 gives zeros, M = 0 or N = 0 gives an empty result.
+* degenerate sizes: K = 0 gives zeros, M = 0 or N = 0 gives an empty result;
+* for the compute-roof probes: closed forms of the multiply-add chain, each
+  step rounded once from the exact rational value, and hand-worked cases of
+  the 32 x 2 by 2 x 32 product.
 """
 from __future__ import annotations
 
@@ -164,3 +167,65 @@ def pin_degenerate(lib):
 
 ALL_PINS = [pin_hand_examples, pin_bruteforce_exact, pin_identity, pin_all_ones,
             pin_integer_library, pin_degenerate]
+
+
+# --- the compute-roof probes' oracle ---------------------------------------
+
+def round_to_f32(q: Fraction) -> np.float32:
+    """Round an exact rational to the nearest float32 (ties to even)."""
+    f = np.float32(float(q))
+    lo, hi = (np.nextafter(f, np.float32(-np.inf)), f) if Fraction(float(f)) > q else \
+             (f, np.nextafter(f, np.float32(np.inf)))
+    dl, dh = q - Fraction(float(lo)), Fraction(float(hi)) - q
+    if dl != dh:
+        return lo if dl < dh else hi
+    return lo if (int(lo.view(np.uint32)) & 1) == 0 else hi
+
+
+def pin_fma_chain_exact_rounding(lib):
+    # Each step is the exact value acc * x + y rounded once to float32.
+    x, y = np.float32(0.999), np.float32(0.001)
+    got = oracle.fma_chain_f32(300, float(x), float(y), 16, lib=lib)
+    for j in range(16):
+        acc = np.float32(0.0625) * np.float32(j + 1)
+        for _ in range(300):
+            acc = round_to_f32(Fraction(float(acc)) * Fraction(float(x)) + Fraction(float(y)))
+        assert got[j] == acc, (j, got[j], acc)
+
+
+def pin_fma_chain_closed_forms(lib):
+    # x = 1, y = 1: each step adds 1 exactly (values stay below 2^24).
+    got = oracle.fma_chain_f32(1000, 1.0, 1.0, 16, lib=lib)
+    assert np.array_equal(got, np.float32(0.0625) * np.arange(1, 17, dtype=np.float32) + 1000), got
+    # x = 2, y = 0: doubling is exact.
+    got = oracle.fma_chain_f32(20, 2.0, 0.0, 16, lib=lib)
+    assert np.array_equal(got, np.float32(0.0625) * np.arange(1, 17, dtype=np.float32) * 2 ** 20), got
+    # x = 0.5, y = 0.5 from a = 1/16: a_n = 1 - (15/16) 2^-n, exact for small n.
+    got = oracle.fma_chain_f32(5, 0.5, 0.5, 1, lib=lib)
+    assert got[0] == np.float32(1 - 15 / 16 * 2 ** -5), got
+    # zero iterations return the starting values.
+    assert np.array_equal(oracle.fma_chain_f32(0, 3.0, 7.0, 4, lib=lib),
+                          np.float32(0.0625) * np.arange(1, 5, dtype=np.float32))
+
+
+def pin_mfma_probe_products(lib):
+    # All ones: every entry is iters * 2 (two k terms).
+    D = oracle.mfma_probe_f64(3, np.ones(64), np.ones(64), lib=lib)
+    assert np.all(D == 6.0)
+    # A[5][0] = 1 (a_vals[5]) and B[0][7] = 1 (b_vals[7]): only D[5][7] = iters.
+    a = np.zeros(64); a[5] = 1
+    b = np.zeros(64); b[7] = 1
+    D = oracle.mfma_probe_f64(9, a, b, lib=lib)
+    want = np.zeros((32, 32)); want[5, 7] = 9
+    assert np.array_equal(D, want)
+    # Mismatched k (A uses k = 0, B uses k = 1): zero.
+    b = np.zeros(64); b[7 + 32] = 1
+    assert np.all(oracle.mfma_probe_f64(9, a, b, lib=lib) == 0)
+    # A[i][1] = a_vals[i + 32], B[1][j] = b_vals[j + 32]: an outer product.
+    a = np.zeros(64); a[32:] = np.arange(32)
+    b = np.zeros(64); b[32:] = np.arange(32) - 16
+    D = oracle.mfma_probe_f64(2, a, b, lib=lib)
+    assert np.array_equal(D, 2 * np.outer(np.arange(32), np.arange(32) - 16))
+
+
+ALL_PINS += [pin_fma_chain_closed_forms, pin_fma_chain_exact_rounding, pin_mfma_probe_products]

@@ -118,3 +118,14 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         rs.sgemm(torch.ones(2, 2), torch.ones(2, 2))
+
+
+def test_probe_validation(lib):
+    assert lib.sgemm_probe_valu_f32(PA, 0, 64, 1, 1.0, 1.0, None) == ARG
+    assert lib.sgemm_probe_valu_f32(PA, 1, 96, 1, 1.0, 1.0, None) == ARG
+    assert lib.sgemm_probe_valu_f32(PA, 1 << 21, 64, 1, 1.0, 1.0, None) == ARG
+    assert lib.sgemm_probe_valu_f32(PA, 1, 64, -1, 1.0, 1.0, None) == ARG
+    assert lib.sgemm_probe_valu_f32(None, 1, 64, 1, 1.0, 1.0, None) == NULLPTR
+    assert lib.sgemm_probe_mfma_f32(PA, None, PB, 1, 1, None) == NULLPTR
+    assert lib.sgemm_probe_mfma_f32(PA, PB, PC, 0, 1, None) == ARG
+    assert lib.sgemm_probe_mfma_f32(PA, PB, PC, 1, -1, None) == ARG

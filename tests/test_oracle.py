@@ -92,6 +92,11 @@ MUTANTS = {
     "bound_signed": ("s[j] += mag * fabs((double)brow[j]);", "s[j] += aik * (double)brow[j];"),
     "entries_drop_first": ("for (int64_t k = 0; k < K; k++) {\n            const double p",
                            "for (int64_t k = 1; k < K; k++) {\n            const double p"),
+    "chain_unfused": ("acc = fmaf(acc, x, y);", "acc = acc * x; acc = acc + y;"),
+    "chain_start": ("float acc = 0.0625f * (float)(j + 1);", "float acc = 0.0625f * (float)j;"),
+    "probe_transposed": ("(double)a_vals[i + 32 * k] * (double)b_vals[j + 32 * k]",
+                         "(double)a_vals[32 * i % 64 + k] * (double)b_vals[j + 32 * k]"),
+    "probe_one_k": ("for (int k = 0; k < 2; k++) p +=", "for (int k = 0; k < 1; k++) p +="),
 }
 
 
