@@ -230,7 +230,7 @@ def ladder(args, out):
     import roofline_sgemm_f32_amd as rs
     names = args.ladder_workloads.split(",")
     variants = ["k0_naive", "k1_coalesced", "k2_lds_tiled16", "k2_lds_tiled32", "k2_lds_tiled32_pad1", "k2_lds_tiled16_pad1",
-                "k3_regtile_db", "k4_mfma", "auto"]
+                "k3_regtile_db", "k4_mfma_tile64", "k4_mfma_tile128", "k4_mfma", "auto"]
     rows = []
     for name in names:
         w = WORKLOADS[name]
@@ -267,8 +267,8 @@ def main():
     from roofline_sgemm_f32_amd.inputs import WORKLOADS
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="square4096", choices=sorted(WORKLOADS))
     p.add_argument("--variant", default="auto")
     p.add_argument("--cpu-seconds", type=float, default=12.0,

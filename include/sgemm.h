@@ -48,18 +48,21 @@ extern "C" {
 /* Kernel ladder.  Every variant computes the same product and accepts every
  * shape the validation above accepts (SGEMM_K4_MFMA excepted, see
  * SGEMM_ERR_UNSUPPORTED); they differ in how they use the chip.  Variants
- * 0-4 are the ladder proper; 5-8 are comparison points. */
+ * 0-4 are the ladder proper; 5-10 are comparison points. */
 typedef enum sgemm_variant {
     SGEMM_AUTO = 0,               /* pick per shape (the matrix-core kernel for large shapes) */
     SGEMM_K1_COALESCED = 1,       /* one output per lane, lanes along a row of C (coalesced B/C, uniform A) */
     SGEMM_K2_LDS_TILED = 2,       /* 32 x 32 LDS tiles of A and B per K step; one output per lane */
     SGEMM_K3_REGTILE_DB = 3,      /* 128 x 128 workgroup tile, 8 x 8 outputs per lane in VGPRs, LDS double buffer */
-    SGEMM_K4_MFMA = 4,            /* FP32 matrix-core kernel (v_mfma_f32_32x32x2_f32), direct global->LDS loads */
+    SGEMM_K4_MFMA = 4,            /* FP32 matrix-core kernel (v_mfma_f32_32x32x2_f32), direct global->LDS
+                                     loads; 128 x 128 or 64 x 64 workgroup tiles chosen by shape */
     SGEMM_K2_LDS_TILED16 = 5,     /* as K2 with 16 x 16 tiles */
     SGEMM_K2_LDS_TILED_PAD1 = 6,  /* as K2 with rows padded by one float (LDS bank comparison) */
     SGEMM_K0_NAIVE = 7,           /* one output per lane, lanes down a column of C (uncoalesced foil) */
     SGEMM_K2_LDS_TILED16_PAD1 = 8,/* as K2_LDS_TILED16 with rows padded by one float */
-    SGEMM_VARIANT_COUNT = 9
+    SGEMM_K4_MFMA_TILE128 = 9,    /* K4 with 128 x 128 tiles whatever the shape */
+    SGEMM_K4_MFMA_TILE64 = 10,    /* K4 with 64 x 64 tiles whatever the shape */
+    SGEMM_VARIANT_COUNT = 11
 } sgemm_variant_t;
 
 typedef enum sgemm_status {

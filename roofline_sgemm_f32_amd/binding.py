@@ -24,6 +24,8 @@ VARIANTS = {
     "k2_lds_tiled32_pad1": 6,
     "k0_naive": 7,
     "k2_lds_tiled16_pad1": 8,
+    "k4_mfma_tile128": 9,
+    "k4_mfma_tile64": 10,
 }
 
 # sgemm_status_t

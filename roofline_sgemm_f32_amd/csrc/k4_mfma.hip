@@ -6,42 +6,25 @@
 // last step of the ladder.  On CDNA4 one v_mfma_f32_32x32x2_f32 multiplies a
 // 32 x 2 slice of A by a 2 x 32 slice of B into a 32 x 32 float accumulator
 // held across the wave's 64 lanes (16 registers per lane), at the same FP32
-// rate as packed vector FMA but from two operand registers per lane.
+// rate as the vector units' peak but from two operand registers per lane.
 //
-// Workgroup: 256 lanes = 4 waves in a 2 x 2 arrangement, tile 128 x 128 of C,
-// K consumed in slabs of 16.  Each wave owns a 64 x 64 sub-tile = 2 x 2
-// MFMA blocks (64 accumulator registers per lane).
-//
-// Global -> LDS: buffer loads that write LDS directly (buffer_load ... lds),
-// so staged data never passes through VGPRs.  Each such load fills a
-// contiguous run of LDS (lane L's bytes at L * size), and the lane chooses
-// which global element it fetches; that choice implements the LDS layouts
-// below.  Elements outside the matrix get an offset past the buffer's range,
-// which the hardware returns as zero: edge tiles and the K tail need no
-// separate path.  With 16-byte aligned operands whose rows and K, N are
-// multiples of 4 floats each lane moves 16 bytes (dwordx4); otherwise 4.
-//
-// LDS layouts (two stages, double buffered, one barrier per slab):
-//   A stage: 128 rows x 16 floats (64 B per row).  The four 16-byte chunks of
-//            row r are stored XOR-permuted by swz(r), so that the eight (or
-//            sixteen) rows read together by a ds_read_b128 land in distinct
-//            banks.
-//   B stage: 16 rows x 128 floats, written as 8 blocks of two rows (1 KiB)
-//            with a 32-byte gap after each block.  Rows k and k+8, read in
-//            the same instruction by the two halves of a wave, then sit 128
-//            bytes apart modulo 256 and hit different banks.
-//
-// MFMA operand mapping.  The 32x32x2 instruction gives lane L the A element
-// (i = L % 32, kslot = L / 32) and the B element (kslot = L / 32, j = L % 32).
-// Which real k a slot stands for is free as long as A and B agree; here
-// kslot s at step t (0..7) is k = 8s + t, so a lane's eight A values of the
-// slab are contiguous (two ds_read_b128) and its B values are single floats
-// of one column.
-//
-// Tile order: workgroups are dealt to the 8 XCDs round-robin by id, so ids
-// are remapped to give each XCD a contiguous range of tiles, and tiles are
-// walked in groups of 8 tile-rows so that concurrently running tiles share A
-// and B panels in that XCD's L2.
+// Structure (geometry and LDS layouts in k4_layout.h):
+//  * a workgroup owns a BM x BN tile of C; each wave TM x TN accumulators;
+//  * K is consumed in slabs of BK, double-buffered in LDS with one barrier
+//    per slab: read this slab's fragments, issue the next slab's loads into
+//    the other stage, run the slab's MFMAs, wait for the loads, barrier;
+//  * global -> LDS uses buffer loads that write LDS directly
+//    (buffer_load_dword[x4] ... lds), so staged data never occupies VGPRs;
+//  * elements outside the matrix get a buffer offset past the descriptor's
+//    range, which the hardware returns as zero: edge tiles and the K tail run
+//    the same code; stores are masked only in edge tiles;
+//  * 16-byte loads when both operands are 16-byte aligned and lda, ldb, K, N
+//    are multiples of 4, else 4-byte loads (same LDS image either way);
+//  * tile order: workgroup ids are dealt to the 8 XCDs round-robin, so ids
+//    are remapped to give each XCD a contiguous range of tiles, walked in
+//    groups of GROUP_M tile-rows so that resident tiles share A and B panels
+//    in that XCD's L2.
+#include "k4_layout.h"
 #include "kernels.h"
 
 namespace sgemm {
@@ -51,18 +34,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int BM = 128, BN = 128, BK = 16;
-constexpr int A_STAGE = BM * BK * 4;           // 8192 bytes
-constexpr int B_BLOCK = 2 * BN * 4;            // two k-rows, 1024 bytes
-constexpr int B_BLOCK_STRIDE = B_BLOCK + 32;   // 1056 bytes
-constexpr int B_STAGE = (BK / 2) * B_BLOCK_STRIDE;
-constexpr int STAGE = A_STAGE + B_STAGE;       // 16640 bytes
 constexpr int GROUP_M = 8;
-constexpr unsigned OOB = 0x80000000u;          // offset the buffer range check rejects
-constexpr int RSRC_WORD3 = 0x00020000;         // raw buffer, 32-bit data format
-
-// Chunk permutation of A row r (4 chunks of 16 bytes per row).
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+constexpr unsigned OOB = 0x80000000u;  // offset the buffer range check rejects
+constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format
+// Largest tile and slab any configuration uses (for the 31-bit offset limit).
+constexpr int MAX_BM = 256, MAX_BN = 256, MAX_BK = 32;
 
 // One buffer load that writes LDS directly: lane L's 16 (or 4) bytes go to
 // lds + 16 L (or 4 L).
@@ -80,66 +56,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 }
 }  // namespace
 
-template <bool VEC>
-__global__ void __launch_bounds__(256)
+template <class CF, int OCC>
+__global__ void __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
         const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
         int64_t tiles_m, int64_t tiles_n, int64_t tiles) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH, AQ = CF::A_QUADS;
+    __shared__ __attribute__((aligned(1024))) char smem[CF::LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
     const int li = lane & 31, ls = lane >> 5;
-
-    // Per-lane global element (row/k for A, k/column for B) of each load
-    // instruction, fixed for the whole kernel.
-    constexpr int NA = VEC ? 2 : 8;  // load instructions per wave per slab, A
-    constexpr int NB = VEC ? 2 : 8;  // and B
-    int a_r[NA], a_k[NA], b_k[NB], b_c[NB];
-    unsigned a_lds[NA], b_lds[NB];
-#pragma unroll
-    for (int q = 0; q < NA; q++) {
-        if (VEC) {
-            const int u = wave * 2 + q;             // 16 rows per instruction
-            const int r = u * 16 + lane / 4, pc = lane % 4;
-            a_r[q] = r;
-            a_k[q] = 4 * (pc ^ swz(r));
-            a_lds[q] = u * 1024;
-        } else {
-            const int u = wave * 8 + q;             // 4 rows per instruction
-            const int p = u * 64 + lane, r = p / 16, qq = p % 16;
-            a_r[q] = r;
-            a_k[q] = 4 * ((qq / 4) ^ swz(r)) + qq % 4;
-            a_lds[q] = u * 256;
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < NB; q++) {
-        if (VEC) {
-            const int u = wave * 2 + q;             // one two-row block per instruction
-            b_k[q] = 2 * u + lane / 32;
-            b_c[q] = (lane % 32) * 4;
-            b_lds[q] = A_STAGE + u * B_BLOCK_STRIDE;
-        } else {
-            const int u = wave * 8 + q;             // a quarter block per instruction
-            const int o = (u % 4) * 256 + lane * 4;
-            b_k[q] = 2 * (u / 4) + o / 512;
-            b_c[q] = (o % 512) / 4;
-            b_lds[q] = A_STAGE + (u / 4) * B_BLOCK_STRIDE + (u % 4) * 256;
-        }
-    }
-
-    // Fragment addresses inside a stage (bytes).
-    int a_frag[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; mb++) {
-        const int r = wm * 64 + mb * 32 + li;
-#pragma unroll
-        for (int q = 0; q < 2; q++) a_frag[mb][q] = r * 64 + (((2 * ls + q) ^ swz(r)) * 16);
-    }
-    int b_frag[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; nb++) b_frag[nb] = A_STAGE + (wn * 64 + nb * 32 + li) * 4;
 
     const bool direct = (int64_t)gridDim.x == tiles;
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
@@ -152,133 +79,154 @@ k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t ld
         const int64_t per_group = (int64_t)GROUP_M * tiles_n;
         const int64_t first_m = (lin / per_group) * GROUP_M;
         const int64_t gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-        const int64_t tile_m = first_m + (lin % per_group) % gsz;
-        const int64_t tile_n = (lin % per_group) / gsz;
-        const int64_t row0 = tile_m * BM, col0 = tile_n * BN;
-
-        // Slab-invariant parts of the load offsets.
-        unsigned a_off[NA], b_off[NB];
-        bool a_ok[NA], b_ok[NB];
-#pragma unroll
-        for (int q = 0; q < NA; q++) {
-            a_ok[q] = row0 + a_r[q] < M;
-            a_off[q] = (unsigned)((a_r[q] * lda + a_k[q]) * 4);
-        }
-#pragma unroll
-        for (int q = 0; q < NB; q++) {
-            b_ok[q] = col0 + b_c[q] < N;
-            b_off[q] = (unsigned)((b_k[q] * ldb + b_c[q]) * 4);
-        }
+        const int64_t row0 = (first_m + (lin % per_group) % gsz) * CF::BM;
+        const int64_t col0 = ((lin % per_group) / gsz) * CF::BN;
 
         auto issue = [&](int64_t k0, int stage) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + row0 * lda + k0);
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + k0 * ldb + col0);
-            char* base = smem + stage * STAGE;
+            char* base = smem + stage * CF::STAGE;
 #pragma unroll
-            for (int q = 0; q < NA; q++) {
-                const unsigned off = (a_ok[q] && k0 + a_k[q] < K) ? a_off[q] : OOB;
-                load_lds<VEC>(ra, base + a_lds[q], off);
+            for (int q = 0; q < CF::A_INSTR_PER_WAVE; q++) {
+                const int u = wave * CF::A_INSTR_PER_WAVE + q;
+                const int r = CF::a_load_row(u, lane), k = CF::a_load_k(u, lane);
+                const bool ok = row0 + r < M && k0 + k < K;
+                load_lds<CF::VEC>(ra, base + u * CF::IB,
+                                  ok ? (unsigned)((r * lda + k) * 4) : OOB);
             }
 #pragma unroll
-            for (int q = 0; q < NB; q++) {
-                const unsigned off = (b_ok[q] && k0 + b_k[q] < K) ? b_off[q] : OOB;
-                load_lds<VEC>(rb, base + b_lds[q], off);
+            for (int q = 0; q < CF::B_INSTR_PER_WAVE; q++) {
+                const int u = wave * CF::B_INSTR_PER_WAVE + q;
+                const int k = CF::b_load_k(u, lane), c = CF::b_load_col(u, lane);
+                const bool ok = k0 + k < K && col0 + c < N;
+                load_lds<CF::VEC>(rb, base + CF::b_load_lds(u),
+                                  ok ? (unsigned)((k * ldb + c) * 4) : OOB);
             }
         };
 
-        v16f acc[2][2];
+        v16f acc[TM][TN];
 #pragma unroll
-        for (int mb = 0; mb < 2; mb++)
+        for (int mb = 0; mb < TM; mb++)
 #pragma unroll
-            for (int nb = 0; nb < 2; nb++)
+            for (int nb = 0; nb < TN; nb++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.0f;
 
-        const int64_t nk = (K + BK - 1) / BK;
+        const int64_t nk = (K + CF::BK - 1) / CF::BK;
         if (nk > 0) issue(0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int64_t s = 0; s < nk; s++) {
-            const char* st = smem + (s & 1) * STAGE;
-            v4f a[2][2];
-            float b[2][8];
+            const char* st = smem + (s & 1) * CF::STAGE;
+            v4f a[TM][AQ];
+            float b[TN][KH];
 #pragma unroll
-            for (int mb = 0; mb < 2; mb++)
+            for (int mb = 0; mb < TM; mb++) {
+                const int row = wm * TM * 32 + mb * 32 + li;
 #pragma unroll
-                for (int q = 0; q < 2; q++) a[mb][q] = *(const v4f*)(st + a_frag[mb][q]);
+                for (int q = 0; q < AQ; q++)
+                    a[mb][q] = *(const v4f*)(st + CF::a_frag(row, ls * AQ + q));
+            }
 #pragma unroll
-            for (int nb = 0; nb < 2; nb++)
+            for (int nb = 0; nb < TN; nb++) {
+                const int col = wn * TN * 32 + nb * 32 + li;
 #pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const int k = ls * 8 + u;
-                    b[nb][u] = *(const float*)(st + b_frag[nb] + (k / 2) * B_BLOCK_STRIDE +
-                                               (k % 2) * (BN * 4));
-                }
+                for (int u = 0; u < KH; u++)
+                    b[nb][u] = *(const float*)(st + CF::b_frag(CF::kslot(ls, u), col));
+            }
             // All reads of this stage are issued before the next slab's
             // loads, which target the other stage.
             asm volatile("" ::: "memory");
-            if (s + 1 < nk) issue((s + 1) * BK, int((s + 1) & 1));
+            if (s + 1 < nk) issue((s + 1) * CF::BK, int((s + 1) & 1));
 #pragma unroll
-            for (int u = 0; u < 8; u++)
+            for (int u = 0; u < KH; u++)
 #pragma unroll
-                for (int mb = 0; mb < 2; mb++)
+                for (int mb = 0; mb < TM; mb++)
 #pragma unroll
-                    for (int nb = 0; nb < 2; nb++)
+                    for (int nb = 0; nb < TN; nb++)
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                             a[mb][u / 4][u % 4], b[nb][u], acc[mb][nb], 0, 0, 0);
             // Register-only MFMAs may otherwise be scheduled after the wait
             // and barrier below, which would expose the load latency; tie
             // the accumulators to this point.
 #pragma unroll
-            for (int mb = 0; mb < 2; mb++)
+            for (int mb = 0; mb < TM; mb++)
 #pragma unroll
-                for (int nb = 0; nb < 2; nb++) asm volatile("" : "+a"(acc[mb][nb]));
+                for (int nb = 0; nb < TN; nb++) asm volatile("" : "+a"(acc[mb][nb]));
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
 
         // Accumulator register r of lane L holds row 8*(r/4) + 4*(L/32) + r%4,
         // column L%32 of its 32 x 32 block.
-        const bool interior = row0 + BM <= M && col0 + BN <= N;
+        const bool interior = row0 + CF::BM <= M && col0 + CF::BN <= N;
 #pragma unroll
-        for (int mb = 0; mb < 2; mb++)
+        for (int mb = 0; mb < TM; mb++)
 #pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
-                const int64_t c = col0 + wn * 64 + nb * 32 + li;
-                float* cp = C + (row0 + wm * 64 + mb * 32 + ls * 4) * ldc + c;
+            for (int nb = 0; nb < TN; nb++) {
+                const int64_t c = col0 + wn * TN * 32 + nb * 32 + li;
+                const int64_t rbase = row0 + wm * TM * 32 + mb * 32 + ls * 4;
+                float* cp = C + rbase * ldc + c;
                 if (interior) {
 #pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        cp[((r / 4) * 8 + (r % 4)) * ldc] = acc[mb][nb][r];
-                } else {
+                    for (int r = 0; r < 16; r++) cp[((r / 4) * 8 + (r % 4)) * ldc] = acc[mb][nb][r];
+                } else if (c < N) {
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int64_t row = row0 + wm * 64 + mb * 32 + (r / 4) * 8 + ls * 4 + (r % 4);
-                        if (row < M && c < N) cp[((r / 4) * 8 + (r % 4)) * ldc] = acc[mb][nb][r];
-                    }
+                    for (int r = 0; r < 16; r++)
+                        if (rbase + (r / 4) * 8 + (r % 4) < M)
+                            cp[((r / 4) * 8 + (r % 4)) * ldc] = acc[mb][nb][r];
                 }
             }
     }
 }
 
+template <class CF, int OCC>
+hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
+    const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
+    hipLaunchKernelGGL((k4_mfma<CF, OCC>), dim3(grid_for(tiles)), dim3(CF::THREADS), 0, s, g.M,
+                       g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, tm, tn, tiles);
+    return hipGetLastError();
+}
+
 bool k4_supports(const GemmArgs& g) {
     // Largest valid byte offset from a slab's base must stay below OOB.
     const int64_t lim = int64_t(OOB) - 64;
-    return ((int64_t)(BM - 1) * g.lda + BK) * 4 < lim && ((int64_t)(BK - 1) * g.ldb + BN) * 4 < lim;
+    return ((int64_t)(MAX_BM - 1) * g.lda + MAX_BK) * 4 < lim &&
+           ((int64_t)(MAX_BK - 1) * g.ldb + MAX_BN) * 4 < lim;
+}
+
+static bool vec_ok(const GemmArgs& g) {
+    return (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) &&
+           (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
+           g.K % 4 == 0 && g.N % 4 == 0;
+}
+
+// Tile configurations (chosen from a sweep over square 256..8192, skinny and
+// unaligned shapes on MI355X):
+//  * 128 x 128 tiles, 4 waves of 2 x 2 accumulators, K slabs of 16, 4 waves
+//    per SIMD: best once there are at least 1024 tiles (4 per CU), e.g.
+//    square 4096 and 8192;
+//  * 64 x 64 tiles, 4 waves of 1 accumulator: below that, the larger tile
+//    count fills the 256 CUs (square 1024: 2.9x faster than 128 x 128);
+//    K slabs of 32 with 16-byte loads, of 16 with 4-byte loads.
+template <bool V> using Tile128 = k4::Cfg<2, 2, 2, 2, 16, V>;
+using Tile64Vec = k4::Cfg<2, 2, 1, 1, 32, true>;
+using Tile64Dword = k4::Cfg<2, 2, 1, 1, 16, false>;
+
+hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
+    if (vec_ok(g)) return launch_k4_cfg<Tile128<true>, 4>(g, s);
+    return launch_k4_cfg<Tile128<false>, 3>(g, s);
+}
+
+hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) {
+    if (vec_ok(g)) return launch_k4_cfg<Tile64Vec, 4>(g, s);
+    return launch_k4_cfg<Tile64Dword, 8>(g, s);
 }
 
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s) {
-    const int64_t tm = ceil_div(g.M, BM), tn = ceil_div(g.N, BN), tiles = tm * tn;
-    const bool vec = (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && g.lda % 4 == 0 &&
-                     g.ldb % 4 == 0 && g.K % 4 == 0 && g.N % 4 == 0;
-    if (vec)
-        hipLaunchKernelGGL(k4_mfma<true>, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K,
-                           g.A, g.lda, g.B, g.ldb, g.C, g.ldc, tm, tn, tiles);
-    else
-        hipLaunchKernelGGL(k4_mfma<false>, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K,
-                           g.A, g.lda, g.B, g.ldb, g.C, g.ldc, tm, tn, tiles);
-    return hipGetLastError();
+    const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
+    if (vec_ok(g) && tiles128 >= 1024) return launch_k4_cfg<Tile128<true>, 4>(g, s);
+    return launch_k4_tile64(g, s);
 }
 
 }  // namespace sgemm

@@ -33,7 +33,9 @@ hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k1_coalesced(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k2_lds(const GemmArgs& g, int tile, int pad, hipStream_t s);
 hipError_t launch_k3_regtile(const GemmArgs& g, hipStream_t s);
-hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s);
+hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s);    // tile size chosen by shape
+hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s);
+hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.
 bool k4_supports(const GemmArgs& g);
 hipError_t launch_zero(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);

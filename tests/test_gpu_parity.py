@@ -21,8 +21,8 @@ from tests.gpu_util import run, to_device
 pytestmark = pytest.mark.gpu
 
 ALL = ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16", "k2_lds_tiled32_pad1", "k2_lds_tiled16_pad1",
-       "k3_regtile_db", "k4_mfma", "auto"]
-FAST = ["k3_regtile_db", "k4_mfma", "auto"]
+       "k3_regtile_db", "k4_mfma", "k4_mfma_tile128", "k4_mfma_tile64", "auto"]
+FAST = ["k3_regtile_db", "k4_mfma", "k4_mfma_tile128", "k4_mfma_tile64", "auto"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -173,12 +173,13 @@ def test_all_ones_gives_row_sums(variant):
     assert np.all(C == C[:, :1])
 
 
-def test_row_permutation_k4():
+@pytest.mark.parametrize("variant", ["k4_mfma_tile128", "k4_mfma_tile64"])
+def test_row_permutation_k4(variant):
     M, N, K = 256, 256, 300
     A, B = make_operands(M, N, K, "normal", seed=41)
     perm = torch.randperm(M, generator=torch.Generator().manual_seed(1))
-    C, _ = run("k4_mfma", A, B)
-    Cp, _ = run("k4_mfma", A[perm].contiguous(), B)
+    C, _ = run(variant, A, B)
+    Cp, _ = run(variant, A[perm].contiguous(), B)
     assert np.array_equal(Cp, C[perm.numpy()])
 
 
@@ -191,7 +192,7 @@ def _sample(n, k, seed):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-@pytest.mark.parametrize("variant", ["auto", "k4_mfma"])
+@pytest.mark.parametrize("variant", ["auto", "k4_mfma_tile128", "k4_mfma_tile64"])
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload(variant, name):
     """The workloads at full size: complete check where the oracle is quick
