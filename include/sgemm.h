@@ -90,6 +90,39 @@ int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K,
                       const float *B, int64_t ldb,
                       float *C, int64_t ldc, void *stream);
 
+/* Operand orientation for the general entry points. */
+typedef enum sgemm_op { SGEMM_OP_N = 0, SGEMM_OP_T = 1 } sgemm_op_t;
+
+/* General form, row-major: C = alpha * op(A) * op(B) + beta * C, with op(A)
+ * M x K and op(B) K x N (the BLAS operation of the course's library call in
+ * amittech.dev, "3.5 Project: tiled matrix multiplication", section "the
+ * reference ceiling", here in row-major storage).
+ *   transa == SGEMM_OP_N: A is stored M x K, lda >= max(1, K);
+ *   transa == SGEMM_OP_T: A is stored K x M, lda >= max(1, M) (op(A) = A^T);
+ *   transb == SGEMM_OP_N: B is stored K x N, ldb >= max(1, N);
+ *   transb == SGEMM_OP_T: B is stored N x K, ldb >= max(1, K);
+ *   ldc >= max(1, N).
+ * beta == 0: C is written without being read (NaN in C does not
+ * propagate).  K == 0 or alpha == 0: A and B are not read and C = beta * C.
+ * C may be read and written in place; it must not overlap A or B when they
+ * are read (SGEMM_ERR_ALIAS).  Other conventions as sgemm_f32; an invalid
+ * transa / transb is SGEMM_ERR_ARG. */
+int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                 const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                 float *C, int64_t ldc, void *stream);
+
+/* The same operation in column-major storage (the BLAS and cuBLAS
+ * convention): C (m x n, ldc >= max(1, m)) = alpha * op(A) op(B) + beta * C,
+ * op(A) m x k, op(B) k x n; A is m x k (lda >= max(1, m)) or, transposed,
+ * k x m (lda >= max(1, k)); B is k x n (ldb >= max(1, k)) or n x k
+ * (ldb >= max(1, n)).  Computed as the row-major product
+ * C^T = op(B)^T op(A)^T, i.e. sgemm_f32_ex(transb, transa, n, m, k, alpha,
+ * B, ldb, A, lda, beta, C, ldc, stream) - the operand swap the course uses
+ * to run its row-major product through a column-major library. */
+int sgemm_f32_colmajor(int transa, int transb, int64_t m, int64_t n, int64_t k, float alpha,
+                       const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                       float *C, int64_t ldc, void *stream);
+
 /* Device-to-device copy dst[i] = src[i], 0 <= i < n, with a grid-stride loop:
  * the HBM bandwidth probe of amittech.dev, "7.3 Bandwidths and peak rate -
  * exercises", exercise 2 (it moves 2 * n * 4 bytes).  dst and src are device

@@ -65,6 +65,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_sgemm_rows_f64.restype = cint
     lib.oracle_sgemm_entries_f64.argtypes = [i64, vp, vp, i64, vp, i64, vp, i64, vp, vp]
     lib.oracle_sgemm_entries_f64.restype = cint
+    lib.oracle_sgemm_ex_f64.argtypes = [cint, cint, i64, i64, i64, ctypes.c_double, vp, i64, vp, i64,
+                                        ctypes.c_double, vp, i64, vp, vp, vp, i64]
+    lib.oracle_sgemm_ex_f64.restype = cint
     lib.oracle_fma_chain_f32.argtypes = [i64, ctypes.c_float, ctypes.c_float, cint, vp]
     lib.oracle_fma_chain_f32.restype = None
     lib.oracle_mfma_probe_f64.argtypes = [i64, vp, vp, vp]
@@ -179,3 +182,28 @@ def mfma_probe_f64(iters: int, a_vals: np.ndarray, b_vals: np.ndarray, lib: ctyp
     D = np.empty((32, 32), dtype=np.float64)
     lib.oracle_mfma_probe_f64(iters, _ptr(a), _ptr(b), _ptr(D))
     return D
+
+
+def sgemm_ex_f64(transa: bool, transb: bool, alpha: float, A: np.ndarray, B: np.ndarray,
+                 beta: float, C0: np.ndarray | None, lib: ctypes.CDLL | None = None):
+    """C = alpha op(A) op(B) + beta C0 in double (row-major).  A is stored
+    M x K (or K x M when transa), B K x N (or N x K when transb).  Returns
+    (C, S, E) with S = |alpha| sum|ab| and E = |alpha sum ab| + |beta C0|."""
+    lib = lib or load()
+    M, K = (A.shape[1], A.shape[0]) if transa else A.shape
+    Kb, N = (B.shape[1], B.shape[0]) if transb else B.shape
+    if Kb != K:
+        raise ValueError("inner dimensions differ")
+    if C0 is None:
+        if beta != 0:
+            raise ValueError("beta != 0 needs C0")
+        C0 = np.zeros((max(M, 1), max(N, 1)), dtype=np.float32)
+    C = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    E = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_sgemm_ex_f64(int(transa), int(transb), M, N, K, float(alpha), _ptr(A), _ld(A, "A"),
+                                 _ptr(B), _ld(B, "B"), float(beta), _ptr(C0), _ld(C0, "C0"),
+                                 _ptr(C), _ptr(S), _ptr(E), max(N, 1))
+    if rc != 0:
+        raise RuntimeError("oracle_sgemm_ex_f64 failed")
+    return C, S, E

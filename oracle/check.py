@@ -54,3 +54,21 @@ def check(C_gpu, C_ref, S, K: int) -> dict:
         "max_abs_err": float(err[~nan].max()) if (~nan).any() else 0.0,
         "max_rel_err_page": float(rel[~nan].max()) if (~nan).any() else 0.0,
     }
+
+
+def check_ex(C_gpu, C_ref, S, E, K: int) -> dict:
+    """Gate for C = alpha op(A) op(B) + beta C0:
+    |C - C_ref| <= 4 K 2^-24 S + 2 * 2^-24 E, where S = |alpha| sum|ab| covers
+    the dot product's accumulation and E = |alpha sum ab| + |beta C0| the
+    final scaling and addition (one rounding each)."""
+    g = np.asarray(C_gpu, dtype=np.float64)
+    r = np.asarray(C_ref, dtype=np.float64)
+    b = SLACK * K * U * np.asarray(S, dtype=np.float64) + 2 * U * np.asarray(E, dtype=np.float64)
+    err = np.abs(g - r)
+    nan = ~np.isfinite(g)
+    viol = nan | (err > b)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        util = np.where(b > 0, err / np.where(b > 0, b, 1.0), np.where(err == 0, 0.0, np.inf))
+    fu = util[~nan]
+    return {"ok": bool(not viol.any()), "n": int(g.size), "n_violations": int(viol.sum()),
+            "n_nonfinite": int(nan.sum()), "max_bound_util": float(fu.max()) if fu.size else 0.0}

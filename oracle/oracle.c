@@ -138,6 +138,41 @@ int oracle_sgemm_entries_f64(int64_t count, const int64_t *rows, const int64_t *
 }
 
 /* ------------------------------------------------------------------------
+ * General form, row-major: C = alpha * op(A) * op(B) + beta * C0, the BLAS
+ * operation of the course's library call (amittech.dev, "3.5 Project: tiled
+ * matrix multiplication", section "the reference ceiling").  op(A) is M x K:
+ * A itself (stored M x K) or, with transa, the transpose of A stored K x M;
+ * op(B) is K x N likewise (stored K x N, or N x K with transb).  With
+ * alpha == 0 or K == 0 the product is not formed; with beta == 0, C0 is not
+ * read.  Also returned: S = |alpha| * sum_k |op(A)[i][k] op(B)[k][j]| and
+ * E = |alpha * sum_k op(A)[i][k] op(B)[k][j]| + |beta * C0[i][j]|, the two
+ * magnitudes the checker's bound scales with.  Plain element-by-element
+ * loops, ascending k, in double.
+ */
+int oracle_sgemm_ex_f64(int transa, int transb, int64_t M, int64_t N, int64_t K, double alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
+                        const float *C0, int64_t ldc0, double *C, double *S, double *E,
+                        int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t j = 0; j < N; j++) {
+            double acc = 0.0, mag = 0.0;
+            if (alpha != 0.0)
+                for (int64_t k = 0; k < K; k++) {
+                    const double a = transa ? (double)A[k * lda + i] : (double)A[i * lda + k];
+                    const double b = transb ? (double)B[j * ldb + k] : (double)B[k * ldb + j];
+                    acc += a * b;
+                    mag += fabs(a * b);
+                }
+            const double c0 = beta != 0.0 ? beta * (double)C0[i * ldc0 + j] : 0.0;
+            C[i * ldc + j] = alpha * acc + c0;
+            S[i * ldc + j] = fabs(alpha) * mag;
+            E[i * ldc + j] = fabs(alpha * acc) + fabs(c0);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Compute-roof probes (amittech.dev, "7.3 Bandwidths and peak rate -
  * exercises", exercise 5).
  *

@@ -38,7 +38,9 @@ STATUS = {
 EXPORTS = ["sgemm_f32", "sgemm_f32_variant", "sgemm_copy_f32", "sgemm_copy_f32_launch",
            "sgemm_status_string", "sgemm_variant_name", "sgemm_auto_variant",
            "sgemm_last_hip_error", "sgemm_abi_version", "sgemm_probe_valu_f32",
-           "sgemm_probe_mfma_f32"]
+           "sgemm_probe_mfma_f32", "sgemm_f32_ex", "sgemm_f32_colmajor"]
+
+OP_N, OP_T = 0, 1
 
 
 class SgemmError(RuntimeError):
@@ -67,6 +69,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_f32.restype = cint
     lib.sgemm_f32_variant.argtypes = [cint, *gemm]
     lib.sgemm_f32_variant.restype = cint
+    f32 = ctypes.c_float
+    ex = [cint, cint, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
+    lib.sgemm_f32_ex.argtypes = ex
+    lib.sgemm_f32_ex.restype = cint
+    lib.sgemm_f32_colmajor.argtypes = ex
+    lib.sgemm_f32_colmajor.restype = cint
     lib.sgemm_copy_f32.argtypes = [vp, vp, i64, vp]
     lib.sgemm_copy_f32.restype = cint
     lib.sgemm_copy_f32_launch.argtypes = [vp, vp, i64, cint, i64, vp]
@@ -152,6 +160,55 @@ def sgemm(A, B, out=None, variant="auto"):
                            out.data_ptr(), ldc, _stream_handle(A.device))
     if st != 0:
         raise SgemmError(st, "sgemm_f32_variant")
+    return out
+
+
+def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0):
+    """C = alpha op(A) op(B) + beta C (row-major float32 GPU tensors).  A is
+    M x K, or K x M with transa (op(A) = A^T); B is K x N, or N x K with
+    transb.  ``out`` holds C (read only when beta != 0); it is allocated when
+    omitted (then beta must be 0)."""
+    import torch
+    if A.device.type != "cuda" or B.device.type != "cuda":
+        raise ValueError("operands must be GPU tensors")
+    M, K = (A.shape[1], A.shape[0]) if transa else tuple(A.shape)
+    Kb, N = (B.shape[1], B.shape[0]) if transb else tuple(B.shape)
+    if Kb != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        if beta != 0:
+            raise ValueError("beta != 0 needs out")
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    st = load().sgemm_f32_ex(int(transa), int(transb), M, N, K, alpha, A.data_ptr(), _ld(A, "A"),
+                             B.data_ptr(), _ld(B, "B"), beta, out.data_ptr(), _ld(out, "out"),
+                             _stream_handle(A.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_f32_ex")
+    return out
+
+
+def _ld_col(t, name):
+    """Leading dimension of a column-major 2-D view (unit row stride)."""
+    import torch
+    if t.dtype != torch.float32 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 tensor")
+    if t.shape[0] > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be column-major (unit row stride)")
+    return max(t.stride(1), t.shape[0], 1) if t.shape[1] > 1 else max(t.shape[0], 1)
+
+
+def sgemm_colmajor(A, B, out, transa=False, transb=False, alpha=1.0, beta=0.0):
+    """The column-major (BLAS) convention on column-major tensor views
+    (stride(0) == 1): out (m x n) = alpha op(A) op(B) + beta out."""
+    m, n = out.shape
+    k = A.shape[0] if transa else A.shape[1]
+    st = load().sgemm_f32_colmajor(int(transa), int(transb), m, n, k, alpha, A.data_ptr(),
+                                   _ld_col(A, "A"), B.data_ptr(), _ld_col(B, "B"), beta,
+                                   out.data_ptr(), _ld_col(out, "out"), _stream_handle(out.device))
+    if st != 0:
+        raise SgemmError(st, "sgemm_f32_colmajor")
     return out
 
 

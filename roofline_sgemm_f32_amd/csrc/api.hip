@@ -49,6 +49,30 @@ int validate(int variant, int64_t M, int64_t N, int64_t K, const float* A, int64
     return SGEMM_OK;
 }
 
+// Validation of the general entry point (row-major; see include/sgemm.h).
+int validate_ex(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                int64_t lda, const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    if ((ta != SGEMM_OP_N && ta != SGEMM_OP_T) || (tb != SGEMM_OP_N && tb != SGEMM_OP_T))
+        return SGEMM_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+    const int64_t lim = int64_t(1) << 40;
+    if (M > lim || N > lim || K > lim) return SGEMM_ERR_DIM;
+    const int64_t m1 = M > 1 ? M : 1, n1 = N > 1 ? N : 1, k1 = K > 1 ? K : 1;
+    if (lda < (ta ? m1 : k1) || ldb < (tb ? k1 : n1) || ldc < n1) return SGEMM_ERR_LD;
+    if (lda > lim || ldb > lim || ldc > lim) return SGEMM_ERR_LD;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return SGEMM_ERR_NULLPTR;
+    if (K > 0 && alpha != 0.0f) {
+        if (A == nullptr || B == nullptr) return SGEMM_ERR_NULLPTR;
+        uintptr_t clo, chi, alo, ahi, blo, bhi;
+        span(C, M, N, ldc, &clo, &chi);
+        if (ta) span(A, K, M, lda, &alo, &ahi); else span(A, M, K, lda, &alo, &ahi);
+        if (tb) span(B, N, K, ldb, &blo, &bhi); else span(B, K, N, ldb, &blo, &bhi);
+        if (overlaps(clo, chi, alo, ahi) || overlaps(clo, chi, blo, bhi)) return SGEMM_ERR_ALIAS;
+    }
+    return SGEMM_OK;
+}
+
 int choose_auto(const GemmArgs& g) {
     // The matrix-core kernel handles every shape whose per-slab offsets fit
     // its 32-bit buffer addressing; the register-tiled kernel (64-bit
@@ -93,6 +117,32 @@ int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float*
 int sgemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
               int64_t ldb, float* C, int64_t ldc, void* stream) {
     return sgemm_f32_variant(SGEMM_AUTO, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                 int64_t ldc, void* stream) {
+    const int v = validate_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f) return launch_status(sgemm::launch_scale(C, M, N, ldc, beta, s));
+    GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
+    g.trans_a = transa == SGEMM_OP_T;
+    g.trans_b = transb == SGEMM_OP_T;
+    g.alpha = alpha;
+    g.beta = beta;
+    if (sgemm::k4_supports(g)) return launch_status(sgemm::launch_k4_mfma(g, s));
+    return launch_status(sgemm::launch_k1_general(g, s));
+}
+
+int sgemm_f32_colmajor(int transa, int transb, int64_t m, int64_t n, int64_t k, float alpha,
+                       const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                       float* C, int64_t ldc, void* stream) {
+    // A column-major m x n matrix read row-major is its transpose, so
+    // C = op(A) op(B) (column-major) is C^T = op(B)^T op(A)^T (row-major):
+    // the operands swap places and keep their transpose flags.
+    return sgemm_f32_ex(transb, transa, n, m, k, alpha, B, ldb, A, lda, beta, C, ldc, stream);
 }
 
 int sgemm_auto_variant(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

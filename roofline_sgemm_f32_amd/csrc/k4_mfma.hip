@@ -58,49 +58,77 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 
 template <class CF, int OCC>
 __global__ void __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
-        const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-        int64_t tiles_m, int64_t tiles_n, int64_t tiles) {
-    constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH, AQ = CF::A_QUADS;
+k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* __restrict__ B,
+        int ldb, float* __restrict__ C, int64_t ldc, float alpha, float beta, int tiles_m,
+        int tiles_n, int tiles) {
+    // 32-bit sizes: the host routes shapes whose sizes, leading dimensions
+    // or slab offsets do not fit (k4_supports) to the 64-bit kernel.
+    constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH;
+    using LA = typename CF::LA;
+    using LB = typename CF::LB;
     __shared__ __attribute__((aligned(1024))) char smem[CF::LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
     const int li = lane & 31, ls = lane >> 5;
 
-    const bool direct = (int64_t)gridDim.x == tiles;
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const bool direct = (int)gridDim.x == tiles;
+    for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
         // XCD-contiguous remap of the workgroup id, then grouped tile order.
-        int64_t lin = t;
+        int lin = t;
         if (direct) {
-            const int64_t q = tiles / 8, rem = tiles % 8, x = t % 8;
+            const int q = tiles / 8, rem = tiles % 8, x = t % 8;
             lin = x * q + (x < rem ? x : rem) + t / 8;
         }
-        const int64_t per_group = (int64_t)GROUP_M * tiles_n;
-        const int64_t first_m = (lin / per_group) * GROUP_M;
-        const int64_t gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-        const int64_t row0 = (first_m + (lin % per_group) % gsz) * CF::BM;
-        const int64_t col0 = ((lin % per_group) / gsz) * CF::BN;
+        const int per_group = GROUP_M * tiles_n;
+        const int first_m = (lin / per_group) * GROUP_M;
+        const int gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+        const int row0 = (first_m + (lin % per_group) % gsz) * CF::BM;
+        const int col0 = ((lin % per_group) / gsz) * CF::BN;
 
-        auto issue = [&](int64_t k0, int stage) {
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + row0 * lda + k0);
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + k0 * ldb + col0);
+        auto issue = [&](int k0, int stage) {
             char* base = smem + stage * CF::STAGE;
+            if constexpr (CF::A_KMAJOR) {  // A stored M x K
+                const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * lda + k0);
 #pragma unroll
-            for (int q = 0; q < CF::A_INSTR_PER_WAVE; q++) {
-                const int u = wave * CF::A_INSTR_PER_WAVE + q;
-                const int r = CF::a_load_row(u, lane), k = CF::a_load_k(u, lane);
-                const bool ok = row0 + r < M && k0 + k < K;
-                load_lds<CF::VEC>(ra, base + u * CF::IB,
-                                  ok ? (unsigned)((r * lda + k) * 4) : OOB);
+                for (int q = 0; q < CF::A_INSTR_PER_WAVE; q++) {
+                    const int u = wave * CF::A_INSTR_PER_WAVE + q;
+                    const int r = LA::load_row(u, lane), k = LA::load_k(u, lane);
+                    const bool ok = row0 + r < M && k0 + k < K;
+                    load_lds<CF::VEC>(ra, base + CF::A_BASE + LA::load_lds(u),
+                                      ok ? (unsigned)(r * lda + k) * 4u : OOB);
+                }
+            } else {  // A stored K x M
+                const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)k0 * lda + row0);
+#pragma unroll
+                for (int q = 0; q < CF::A_INSTR_PER_WAVE; q++) {
+                    const int u = wave * CF::A_INSTR_PER_WAVE + q;
+                    const int k = LA::load_k(u, lane), c = LA::load_col(u, lane);
+                    const bool ok = k0 + k < K && row0 + c < M;
+                    load_lds<CF::VEC>(ra, base + CF::A_BASE + LA::load_lds(u),
+                                      ok ? (unsigned)(k * lda + c) * 4u : OOB);
+                }
             }
+            if constexpr (CF::B_KMAJOR) {  // B stored N x K
+                const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)col0 * ldb + k0);
 #pragma unroll
-            for (int q = 0; q < CF::B_INSTR_PER_WAVE; q++) {
-                const int u = wave * CF::B_INSTR_PER_WAVE + q;
-                const int k = CF::b_load_k(u, lane), c = CF::b_load_col(u, lane);
-                const bool ok = k0 + k < K && col0 + c < N;
-                load_lds<CF::VEC>(rb, base + CF::b_load_lds(u),
-                                  ok ? (unsigned)((k * ldb + c) * 4) : OOB);
+                for (int q = 0; q < CF::B_INSTR_PER_WAVE; q++) {
+                    const int u = wave * CF::B_INSTR_PER_WAVE + q;
+                    const int r = LB::load_row(u, lane), k = LB::load_k(u, lane);
+                    const bool ok = col0 + r < N && k0 + k < K;
+                    load_lds<CF::VEC>(rb, base + CF::B_BASE + LB::load_lds(u),
+                                      ok ? (unsigned)(r * ldb + k) * 4u : OOB);
+                }
+            } else {  // B stored K x N
+                const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (int64_t)k0 * ldb + col0);
+#pragma unroll
+                for (int q = 0; q < CF::B_INSTR_PER_WAVE; q++) {
+                    const int u = wave * CF::B_INSTR_PER_WAVE + q;
+                    const int k = LB::load_k(u, lane), c = LB::load_col(u, lane);
+                    const bool ok = k0 + k < K && col0 + c < N;
+                    load_lds<CF::VEC>(rb, base + CF::B_BASE + LB::load_lds(u),
+                                      ok ? (unsigned)(k * ldb + c) * 4u : OOB);
+                }
             }
         };
 
@@ -112,27 +140,46 @@ k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t ld
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.0f;
 
-        const int64_t nk = (K + CF::BK - 1) / CF::BK;
+        const int nk = (K + CF::BK - 1) / CF::BK;
         if (nk > 0) issue(0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        for (int64_t s = 0; s < nk; s++) {
+        for (int s = 0; s < nk; s++) {
             const char* st = smem + (s & 1) * CF::STAGE;
-            v4f a[TM][AQ];
-            float b[TN][KH];
+            // Lane (li, ls) supplies A[row][kslot(ls, u)] and B[kslot(ls, u)][col]
+            // for the slab's KH steps u.
+            float af[TM][KH], bf[TN][KH];
 #pragma unroll
             for (int mb = 0; mb < TM; mb++) {
                 const int row = wm * TM * 32 + mb * 32 + li;
+                if constexpr (CF::A_KMAJOR) {
 #pragma unroll
-                for (int q = 0; q < AQ; q++)
-                    a[mb][q] = *(const v4f*)(st + CF::a_frag(row, ls * AQ + q));
+                    for (int q = 0; q < KH / 4; q++) {
+                        const v4f v = *(const v4f*)(st + CF::a_elem(row, CF::kslot(ls, 4 * q)));
+#pragma unroll
+                        for (int e = 0; e < 4; e++) af[mb][4 * q + e] = v[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < KH; u++)
+                        af[mb][u] = *(const float*)(st + CF::a_elem(row, CF::kslot(ls, u)));
+                }
             }
 #pragma unroll
             for (int nb = 0; nb < TN; nb++) {
                 const int col = wn * TN * 32 + nb * 32 + li;
+                if constexpr (CF::B_KMAJOR) {
 #pragma unroll
-                for (int u = 0; u < KH; u++)
-                    b[nb][u] = *(const float*)(st + CF::b_frag(CF::kslot(ls, u), col));
+                    for (int q = 0; q < KH / 4; q++) {
+                        const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, 4 * q), col));
+#pragma unroll
+                        for (int e = 0; e < 4; e++) bf[nb][4 * q + e] = v[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < KH; u++)
+                        bf[nb][u] = *(const float*)(st + CF::b_elem(CF::kslot(ls, u), col));
+                }
             }
             // All reads of this stage are issued before the next slab's
             // loads, which target the other stage.
@@ -144,8 +191,8 @@ k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t ld
                 for (int mb = 0; mb < TM; mb++)
 #pragma unroll
                     for (int nb = 0; nb < TN; nb++)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            a[mb][u / 4][u % 4], b[nb][u], acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb][u], bf[nb][u],
+                                                                           acc[mb][nb], 0, 0, 0);
             // Register-only MFMAs may otherwise be scheduled after the wait
             // and barrier below, which would expose the load latency; tie
             // the accumulators to this point.
@@ -158,23 +205,31 @@ k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t ld
         }
 
         // Accumulator register r of lane L holds row 8*(r/4) + 4*(L/32) + r%4,
-        // column L%32 of its 32 x 32 block.
+        // column L%32 of its 32 x 32 block.  C = alpha * acc (+ beta * C when
+        // beta is nonzero; C is not read otherwise).
         const bool interior = row0 + CF::BM <= M && col0 + CF::BN <= N;
+        const bool read_c = beta != 0.0f;
 #pragma unroll
         for (int mb = 0; mb < TM; mb++)
 #pragma unroll
             for (int nb = 0; nb < TN; nb++) {
-                const int64_t c = col0 + wn * TN * 32 + nb * 32 + li;
-                const int64_t rbase = row0 + wm * TM * 32 + mb * 32 + ls * 4;
-                float* cp = C + rbase * ldc + c;
-                if (interior) {
-#pragma unroll
-                    for (int r = 0; r < 16; r++) cp[((r / 4) * 8 + (r % 4)) * ldc] = acc[mb][nb][r];
-                } else if (c < N) {
+                const int c = col0 + wn * TN * 32 + nb * 32 + li;
+                const int rbase = row0 + wm * TM * 32 + mb * 32 + ls * 4;
+                float* cp = C + (int64_t)rbase * ldc + c;
+                if (interior && !read_c) {
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        if (rbase + (r / 4) * 8 + (r % 4) < M)
-                            cp[((r / 4) * 8 + (r % 4)) * ldc] = acc[mb][nb][r];
+                        cp[(int64_t)((r / 4) * 8 + (r % 4)) * ldc] = alpha * acc[mb][nb][r];
+                } else if (c < N) {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int dr = (r / 4) * 8 + (r % 4);
+                        if (rbase + dr < M) {
+                            float v = alpha * acc[mb][nb][r];
+                            if (read_c) v = fmaf(beta, cp[(int64_t)dr * ldc], v);
+                            cp[(int64_t)dr * ldc] = v;
+                        }
+                    }
                 }
             }
     }
@@ -183,22 +238,43 @@ k4_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t ld
 template <class CF, int OCC>
 hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
-    hipLaunchKernelGGL((k4_mfma<CF, OCC>), dim3(grid_for(tiles)), dim3(CF::THREADS), 0, s, g.M,
-                       g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, tm, tn, tiles);
+    hipLaunchKernelGGL((k4_mfma<CF, OCC>), dim3(grid_for(tiles)), dim3(CF::THREADS), 0, s,
+                       (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, g.C, g.ldc,
+                       g.alpha, g.beta, (int)tm, (int)tn, (int)tiles);
     return hipGetLastError();
 }
 
-bool k4_supports(const GemmArgs& g) {
-    // Largest valid byte offset from a slab's base must stay below OOB.
+// The four storage orientations of (A, B) for one tile configuration.
+template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC>
+hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s) {
+    if (!g.trans_a && !g.trans_b) return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, true, false>, OCC>(g, s);
+    if (!g.trans_a && g.trans_b) return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, true, true>, OCC>(g, s);
+    if (g.trans_a && !g.trans_b) return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, false, false>, OCC>(g, s);
+    return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, false, true>, OCC>(g, s);
+}
+
+// Largest byte offset a slab reaches from its base, per operand orientation.
+static bool offsets_fit(bool k_major, int64_t ld) {
     const int64_t lim = int64_t(OOB) - 64;
-    return ((int64_t)(MAX_BM - 1) * g.lda + MAX_BK) * 4 < lim &&
-           ((int64_t)(MAX_BK - 1) * g.ldb + MAX_BN) * 4 < lim;
+    return k_major ? ((int64_t)(MAX_BM - 1) * ld + MAX_BK) * 4 < lim
+                   : ((int64_t)(MAX_BK - 1) * ld + MAX_BN) * 4 < lim;
+}
+
+bool k4_supports(const GemmArgs& g) {
+    // 32-bit sizes and tile counts (with room for a tile's overhang), and
+    // slab offsets inside the buffer range.
+    const int64_t lim = (int64_t(1) << 31) - 1024;
+    const int64_t tiles = ceil_div(g.M, 32) * ceil_div(g.N, 32);
+    return g.M < lim && g.N < lim && g.K < lim && g.lda < lim && g.ldb < lim && tiles < lim &&
+           offsets_fit(!g.trans_a, g.lda) && offsets_fit(g.trans_b, g.ldb);
 }
 
 static bool vec_ok(const GemmArgs& g) {
+    // 16-byte loads run along each operand's contiguous dimension.
+    const int64_t a_run = g.trans_a ? g.M : g.K, b_run = g.trans_b ? g.K : g.N;
     return (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) &&
            (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
-           g.K % 4 == 0 && g.N % 4 == 0;
+           a_run % 4 == 0 && b_run % 4 == 0;
 }
 
 // Tile configurations (chosen from a sweep over square 256..8192, skinny and
@@ -209,23 +285,19 @@ static bool vec_ok(const GemmArgs& g) {
 //  * 64 x 64 tiles, 4 waves of 1 accumulator: below that, the larger tile
 //    count fills the 256 CUs (square 1024: 2.9x faster than 128 x 128);
 //    K slabs of 32 with 16-byte loads, of 16 with 4-byte loads.
-template <bool V> using Tile128 = k4::Cfg<2, 2, 2, 2, 16, V>;
-using Tile64Vec = k4::Cfg<2, 2, 1, 1, 32, true>;
-using Tile64Dword = k4::Cfg<2, 2, 1, 1, 16, false>;
-
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_cfg<Tile128<true>, 4>(g, s);
-    return launch_k4_cfg<Tile128<false>, 3>(g, s);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
+    return launch_k4_orient<2, 2, 2, 2, 16, false, 3>(g, s);
 }
 
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_cfg<Tile64Vec, 4>(g, s);
-    return launch_k4_cfg<Tile64Dword, 8>(g, s);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4>(g, s);
+    return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s);
 }
 
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s) {
     const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
-    if (vec_ok(g) && tiles128 >= 1024) return launch_k4_cfg<Tile128<true>, 4>(g, s);
+    if (vec_ok(g) && tiles128 >= 1024) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
     return launch_k4_tile64(g, s);
 }
 

@@ -89,6 +89,55 @@ k2_lds(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda
     }
 }
 
+// The general form C = alpha op(A) op(B) + beta C with k1's mapping (lanes
+// along a row of C) and 64-bit offsets everywhere; it serves the shapes
+// whose per-slab offsets the matrix-core kernel's 32-bit buffer addressing
+// cannot reach.
+__global__ void __launch_bounds__(256)
+k1_general(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+           const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+           bool ta, bool tb, float alpha, float beta, int64_t tiles_n, int64_t tiles) {
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t row = (t / tiles_n) * 4 + wave;
+        const int64_t col = (t % tiles_n) * 64 + lane;
+        if (row < M && col < N) {
+            const int64_t a_step = ta ? lda : 1, b_step = tb ? 1 : ldb;
+            const float* a = A + (ta ? row : row * lda);
+            const float* b = B + (tb ? col * ldb : col);
+            float sum = 0.0f;
+            for (int64_t k = 0; k < K; k++) sum += a[k * a_step] * b[k * b_step];
+            float v = alpha * sum;
+            if (beta != 0.0f) v = fmaf(beta, C[row * ldc + col], v);
+            C[row * ldc + col] = v;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+scale_c(float* __restrict__ C, int64_t M, int64_t N, int64_t ldc, float beta) {
+    const int64_t total = M * N, stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        float* p = C + (i / N) * ldc + (i % N);
+        *p = beta == 0.0f ? 0.0f : beta * *p;
+    }
+}
+
+hipError_t launch_k1_general(const GemmArgs& g, hipStream_t s) {
+    const int64_t tn = ceil_div(g.N, 64), tiles = tn * ceil_div(g.M, 4);
+    hipLaunchKernelGGL(k1_general, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K, g.A,
+                       g.lda, g.B, g.ldb, g.C, g.ldc, g.trans_a, g.trans_b, g.alpha, g.beta, tn,
+                       tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta, hipStream_t s) {
+    hipLaunchKernelGGL(scale_c, dim3(grid_for(ceil_div(M * N, 256))), dim3(256), 0, s, C, M, N, ldc,
+                       beta);
+    return hipGetLastError();
+}
+
 hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, 16), tiles = tm * ceil_div(g.N, 16);
     hipLaunchKernelGGL(k0_naive, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K, g.A,

@@ -7,6 +7,9 @@
 
 namespace sgemm {
 
+// C = alpha * op(A) * op(B) + beta * C, row-major.  trans_a: A is stored
+// K x M (else M x K); trans_b: B is stored N x K (else K x N).  beta == 0
+// means C is not read.
 struct GemmArgs {
     int64_t M, N, K;
     const float* A;
@@ -15,6 +18,8 @@ struct GemmArgs {
     int64_t ldb;
     float* C;
     int64_t ldc;
+    bool trans_a = false, trans_b = false;
+    float alpha = 1.0f, beta = 0.0f;
 };
 
 // Upper bound on the number of workgroups a launch uses; kernels loop over
@@ -39,6 +44,11 @@ hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.
 bool k4_supports(const GemmArgs& g);
 hipError_t launch_zero(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
+// C = beta * C (zeros when beta == 0, C then not read).
+hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta, hipStream_t s);
+// General (transposes, alpha, beta) one-output-per-lane kernel with 64-bit
+// offsets: the fallback for shapes the matrix-core kernel cannot address.
+hipError_t launch_k1_general(const GemmArgs& g, hipStream_t s);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, int block, int64_t grid, hipStream_t s);
 int64_t copy_default_grid(int64_t n, int block);
 hipError_t launch_probe_valu(float* out, int64_t iters, float x, float y, int64_t blocks, int block,

@@ -229,3 +229,63 @@ def pin_mfma_probe_products(lib):
 
 
 ALL_PINS += [pin_fma_chain_closed_forms, pin_fma_chain_exact_rounding, pin_mfma_probe_products]
+
+
+# --- the general form C = alpha op(A) op(B) + beta C0 ----------------------
+
+def _ex_cases():
+    # (transa, transb, alpha, beta)
+    for ta in (False, True):
+        for tb in (False, True):
+            for alpha, beta in ((1.0, 0.0), (2.0, 1.0), (-3.0, -0.5), (0.0, 2.0)):
+                yield ta, tb, alpha, beta
+
+
+def pin_ex_integer_library(lib):
+    # Integer operands: the product is exact, so it must equal numpy's exact
+    # int64 product of the transposed/untransposed operands, scaled and added.
+    M, N, K = 13, 11, 17
+    for t, (ta, tb, alpha, beta) in enumerate(_ex_cases()):
+        A, B = make_operands(M, N, K, "int", seed=300 + t)
+        A, B = as_numpy(A), as_numpy(B)
+        C0 = as_numpy(make_operands(M, 1, N, "int", seed=400 + t)[0])  # an M x N integer matrix
+        As = np.ascontiguousarray(A.T) if ta else A  # stored form
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        got, S, E = oracle.sgemm_ex_f64(ta, tb, alpha, As, Bs, beta, C0, lib=lib)
+        prod = np.matmul(A.astype(np.int64), B.astype(np.int64)).astype(np.float64)
+        want = alpha * prod + beta * C0.astype(np.float64) if beta != 0 else alpha * prod
+        if alpha == 0:
+            want = beta * C0.astype(np.float64)
+        assert np.array_equal(got, want), (ta, tb, alpha, beta)
+        mag = np.matmul(np.abs(A.astype(np.int64)), np.abs(B.astype(np.int64))).astype(np.float64)
+        assert np.array_equal(S, abs(alpha) * mag if alpha != 0 else np.zeros_like(mag)), "S"
+        assert np.array_equal(E, np.abs(want - (beta * C0 if beta != 0 else 0)) + np.abs(beta * C0 if beta != 0 else 0)), "E"
+
+
+def pin_ex_hand_transposed(lib):
+    # op(A) = A^T with A stored 2 x 3 = [[1, 2, 3], [4, 5, 6]] -> op(A) 3 x 2;
+    # op(B) = B^T with B stored 2 x 2 = [[1, 0], [1, 1]] -> op(B) = [[1, 1], [0, 1]].
+    # op(A) op(B) = [[1, 1+4], [2, 2+5], [3, 3+6]] = [[1, 5], [2, 7], [3, 9]];
+    # times alpha = 2, plus beta = 1 times C0 = ones: [[3, 11], [5, 15], [7, 19]].
+    A = np.array([[1, 2, 3], [4, 5, 6]], np.float32)
+    B = np.array([[1, 0], [1, 1]], np.float32)
+    got, _, _ = oracle.sgemm_ex_f64(True, True, 2.0, A, B, 1.0, np.ones((3, 2), np.float32), lib=lib)
+    assert np.array_equal(got, [[3, 11], [5, 15], [7, 19]]), got
+
+
+def pin_ex_unread_operands(lib):
+    # beta == 0: C0 is not read (NaN there does not propagate);
+    # alpha == 0: A and B are not read.
+    A, B = make_operands(5, 6, 7, "uniform", seed=500)
+    A, B = as_numpy(A), as_numpy(B)
+    nan_c = np.full((5, 6), np.nan, np.float32)
+    got, _, _ = oracle.sgemm_ex_f64(False, False, 1.0, A, B, 0.0, nan_c, lib=lib)
+    assert np.isfinite(got).all()
+    nan_a = np.full((5, 7), np.nan, np.float32)
+    nan_b = np.full((7, 6), np.nan, np.float32)
+    C0 = np.arange(30, dtype=np.float32).reshape(5, 6)
+    got, _, _ = oracle.sgemm_ex_f64(False, False, 0.0, nan_a, nan_b, 3.0, C0, lib=lib)
+    assert np.array_equal(got, 3.0 * C0.astype(np.float64))
+
+
+ALL_PINS += [pin_ex_integer_library, pin_ex_hand_transposed, pin_ex_unread_operands]

@@ -129,3 +129,39 @@ def test_probe_validation(lib):
     assert lib.sgemm_probe_mfma_f32(PA, None, PB, 1, 1, None) == NULLPTR
     assert lib.sgemm_probe_mfma_f32(PA, PB, PC, 0, 1, None) == ARG
     assert lib.sgemm_probe_mfma_f32(PA, PB, PC, 1, -1, None) == ARG
+
+
+def ex(ta, tb, M, N, K, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, beta=0.0, C=PC, ldc=None, lib=None):
+    lda = (max(M, 1) if ta else max(K, 1)) if lda is None else lda
+    ldb = (max(K, 1) if tb else max(N, 1)) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return rs.load().sgemm_f32_ex(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+
+
+def test_ex_validation(lib):
+    assert ex(2, 0, 4, 4, 4) == ARG and ex(0, -1, 4, 4, 4) == ARG
+    assert ex(0, 0, -1, 4, 4) == DIM
+    # Leading dimensions follow the stored shapes.
+    assert ex(0, 0, 4, 5, 6, lda=5) == LD      # A M x K needs lda >= K
+    assert ex(1, 0, 4, 5, 6, lda=3) == LD      # A K x M needs lda >= M
+    assert ex(0, 0, 4, 5, 6, ldb=4) == LD      # B K x N needs ldb >= N
+    assert ex(0, 1, 4, 5, 6, ldb=5) == LD      # B N x K needs ldb >= K
+    assert ex(0, 0, 4, 5, 6, ldc=4) == LD
+    assert ex(0, 0, 4, 5, 6, C=None) == NULLPTR
+    assert ex(0, 0, 4, 5, 6, A=None) == NULLPTR
+    assert ex(0, 0, 0, 5, 6, A=None, B=None, C=None) == OK
+    # Output overlapping a read operand.
+    assert ex(0, 0, 4, 5, 6, C=PA + 8) == ALIAS
+    assert ex(1, 1, 4, 5, 6, C=PB) == ALIAS
+
+
+def test_colmajor_maps_to_swapped_rowmajor(lib):
+    # Column-major validation is the swapped row-major one: ldc >= m, and
+    # op(A) m x k with A stored m x k needs lda >= m.
+    f = rs.load().sgemm_f32_colmajor
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 3, PB, 6, 0.0, PC, 4, None) == LD   # lda < m
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 4, PB, 5, 0.0, PC, 4, None) == LD   # ldb < k
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 4, PB, 6, 0.0, PC, 3, None) == LD   # ldc < m
+    assert f(1, 0, 4, 5, 6, 1.0, PA, 5, PB, 6, 0.0, PC, 4, None) == LD   # A k x m: lda >= k
+    assert f(0, 1, 4, 5, 6, 1.0, PA, 4, PB, 4, 0.0, PC, 4, None) == LD   # B n x k: ldb >= n
+    assert f(3, 0, 4, 5, 6, 1.0, PA, 4, PB, 6, 0.0, PC, 4, None) == ARG

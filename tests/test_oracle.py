@@ -97,6 +97,11 @@ MUTANTS = {
     "probe_transposed": ("(double)a_vals[i + 32 * k] * (double)b_vals[j + 32 * k]",
                          "(double)a_vals[32 * i % 64 + k] * (double)b_vals[j + 32 * k]"),
     "probe_one_k": ("for (int k = 0; k < 2; k++) p +=", "for (int k = 0; k < 1; k++) p +="),
+    "ex_transa_index": ("transa ? (double)A[k * lda + i]", "transa ? (double)A[i * lda + k]"),
+    "ex_transb_index": ("transb ? (double)B[j * ldb + k]", "transb ? (double)B[k * ldb + j]"),
+    "ex_beta_dropped": ("const double c0 = beta != 0.0 ? beta * (double)C0[i * ldc0 + j] : 0.0;",
+                        "const double c0 = 0.0;"),
+    "ex_alpha_on_c0": ("C[i * ldc + j] = alpha * acc + c0;", "C[i * ldc + j] = alpha * (acc + c0);"),
 }
 
 
