@@ -56,7 +56,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 }
 }  // namespace
 
-template <class CF, int OCC>
+template <class CF, int OCC, int GM = GROUP_M, bool XCD_REMAP = true, bool SPLIT = false>
 __global__ void __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* __restrict__ B,
         int ldb, float* __restrict__ C, int64_t ldc, float alpha, float beta, int tiles_m,
@@ -72,7 +72,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
     const int li = lane & 31, ls = lane >> 5;
 
-    const bool direct = (int)gridDim.x == tiles;
+    const bool direct = XCD_REMAP && (int)gridDim.x == tiles;
     for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
         // XCD-contiguous remap of the workgroup id, then grouped tile order.
         int lin = t;
@@ -80,9 +80,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             const int q = tiles / 8, rem = tiles % 8, x = t % 8;
             lin = x * q + (x < rem ? x : rem) + t / 8;
         }
-        const int per_group = GROUP_M * tiles_n;
-        const int first_m = (lin / per_group) * GROUP_M;
-        const int gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+        const int per_group = GM * tiles_n;
+        const int first_m = (lin / per_group) * GM;
+        const int gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
         const int row0 = (first_m + (lin % per_group) % gsz) * CF::BM;
         const int col0 = ((lin % per_group) / gsz) * CF::BN;
 
@@ -148,51 +148,66 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             const char* st = smem + (s & 1) * CF::STAGE;
             // Lane (li, ls) supplies A[row][kslot(ls, u)] and B[kslot(ls, u)][col]
             // for the slab's KH steps u.
-            float af[TM][KH], bf[TN][KH];
+            // Fragments are read and consumed in NH parts of KH / NH steps;
+            // with NH = 2 only half of them are live at a time.
+            constexpr int NH = SPLIT ? 2 : 1, KP = KH / NH;
+            auto read_frags = [&](int h, float (&af)[TM][KP], float (&bf)[TN][KP]) {
 #pragma unroll
-            for (int mb = 0; mb < TM; mb++) {
-                const int row = wm * TM * 32 + mb * 32 + li;
-                if constexpr (CF::A_KMAJOR) {
+                for (int mb = 0; mb < TM; mb++) {
+                    const int row = wm * TM * 32 + mb * 32 + li;
+                    if constexpr (CF::A_KMAJOR) {
 #pragma unroll
-                    for (int q = 0; q < KH / 4; q++) {
-                        const v4f v = *(const v4f*)(st + CF::a_elem(row, CF::kslot(ls, 4 * q)));
+                        for (int q = 0; q < KP / 4; q++) {
+                            const v4f v = *(const v4f*)(st + CF::a_elem(row, CF::kslot(ls, h * KP + 4 * q)));
 #pragma unroll
-                        for (int e = 0; e < 4; e++) af[mb][4 * q + e] = v[e];
+                            for (int e = 0; e < 4; e++) af[mb][4 * q + e] = v[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < KP; u++)
+                            af[mb][u] = *(const float*)(st + CF::a_elem(row, CF::kslot(ls, h * KP + u)));
                     }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < KH; u++)
-                        af[mb][u] = *(const float*)(st + CF::a_elem(row, CF::kslot(ls, u)));
                 }
-            }
 #pragma unroll
-            for (int nb = 0; nb < TN; nb++) {
-                const int col = wn * TN * 32 + nb * 32 + li;
-                if constexpr (CF::B_KMAJOR) {
+                for (int nb = 0; nb < TN; nb++) {
+                    const int col = wn * TN * 32 + nb * 32 + li;
+                    if constexpr (CF::B_KMAJOR) {
 #pragma unroll
-                    for (int q = 0; q < KH / 4; q++) {
-                        const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, 4 * q), col));
+                        for (int q = 0; q < KP / 4; q++) {
+                            const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, h * KP + 4 * q), col));
 #pragma unroll
-                        for (int e = 0; e < 4; e++) bf[nb][4 * q + e] = v[e];
+                            for (int e = 0; e < 4; e++) bf[nb][4 * q + e] = v[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < KP; u++)
+                            bf[nb][u] = *(const float*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), col));
                     }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < KH; u++)
-                        bf[nb][u] = *(const float*)(st + CF::b_elem(CF::kslot(ls, u), col));
                 }
-            }
-            // All reads of this stage are issued before the next slab's
-            // loads, which target the other stage.
+            };
+            auto mfmas = [&](const float (&af)[TM][KP], const float (&bf)[TN][KP]) {
+#pragma unroll
+                for (int u = 0; u < KP; u++)
+#pragma unroll
+                    for (int mb = 0; mb < TM; mb++)
+#pragma unroll
+                        for (int nb = 0; nb < TN; nb++)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb][u], bf[nb][u],
+                                                                               acc[mb][nb], 0, 0, 0);
+            };
+            float af[TM][KP], bf[TN][KP];
+            read_frags(0, af, bf);
+            // The next slab's loads target the other stage; issue them once
+            // the first reads of this stage are out.
             asm volatile("" ::: "memory");
             if (s + 1 < nk) issue((s + 1) * CF::BK, int((s + 1) & 1));
+            mfmas(af, bf);
 #pragma unroll
-            for (int u = 0; u < KH; u++)
-#pragma unroll
-                for (int mb = 0; mb < TM; mb++)
-#pragma unroll
-                    for (int nb = 0; nb < TN; nb++)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb][u], bf[nb][u],
-                                                                           acc[mb][nb], 0, 0, 0);
+            for (int h = 1; h < NH; h++) {
+                __builtin_amdgcn_sched_barrier(0);
+                read_frags(h, af, bf);
+                mfmas(af, bf);
+            }
             // Register-only MFMAs may otherwise be scheduled after the wait
             // and barrier below, which would expose the load latency; tie
             // the accumulators to this point.
@@ -235,22 +250,27 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     }
 }
 
-template <class CF, int OCC>
+template <class CF, int OCC, bool SPLIT = false>
 hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
-    hipLaunchKernelGGL((k4_mfma<CF, OCC>), dim3(grid_for(tiles)), dim3(CF::THREADS), 0, s,
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT>), dim3(grid_for(tiles)),
+                       dim3(CF::THREADS), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, g.C, g.ldc,
                        g.alpha, g.beta, (int)tm, (int)tn, (int)tiles);
     return hipGetLastError();
 }
 
 // The four storage orientations of (A, B) for one tile configuration.
-template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC>
+template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s) {
-    if (!g.trans_a && !g.trans_b) return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, true, false>, OCC>(g, s);
-    if (!g.trans_a && g.trans_b) return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, true, true>, OCC>(g, s);
-    if (g.trans_a && !g.trans_b) return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, false, false>, OCC>(g, s);
-    return launch_k4_cfg<k4::Cfg<WM, WN, TM, TN, BK, V, false, true>, OCC>(g, s);
+    using k4::Cfg;
+    if (!g.trans_a && !g.trans_b)
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false>, OCC, SPLIT>(g, s);
+    if (!g.trans_a && g.trans_b)
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true>, OCC, SPLIT>(g, s);
+    if (g.trans_a && !g.trans_b)
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false>, OCC, SPLIT>(g, s);
+    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true>, OCC, SPLIT>(g, s);
 }
 
 // Largest byte offset a slab reaches from its base, per operand orientation.
@@ -284,14 +304,15 @@ static bool vec_ok(const GemmArgs& g) {
 //    square 4096 and 8192;
 //  * 64 x 64 tiles, 4 waves of 1 accumulator: below that, the larger tile
 //    count fills the 256 CUs (square 1024: 2.9x faster than 128 x 128);
-//    K slabs of 32 with 16-byte loads, of 16 with 4-byte loads.
+//    K slabs of 32 with 16-byte loads (fragments read in two halves: another
+//    7 % on square 1024), of 16 with 4-byte loads.
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
     if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
     return launch_k4_orient<2, 2, 2, 2, 16, false, 3>(g, s);
 }
 
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4>(g, s);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s);
     return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s);
 }
 
