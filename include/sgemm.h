@@ -111,6 +111,42 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
                  const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
                  float *C, int64_t ldc, void *stream);
 
+/* sgemm_f32_ex with a K-split request: the small-shape path.  Workgroups
+ * are dealt from a queue to compute units with free resources, and the grid
+ * size does not by itself occupy the chip (qsysarch.com "gemm-kernels",
+ * section "Understanding the naive matrix multiplier"): an output of few
+ * 64 x 64 tiles leaves most of the 256 compute units idle however long K is.
+ * Split-K cuts K into chunks of whole slabs that run as separate workgroups;
+ * each stores its partial product to a workspace of (chunks x M x N) floats,
+ * and a second kernel adds the partials in chunk order and applies alpha and
+ * beta.  The workspace is allocated stream-ordered on `stream` from a memory
+ * pool the library keeps per device (up to 256 MiB stays reserved between
+ * calls) and released on `stream` after the second kernel; if it cannot be
+ * allocated the product runs unsplit.
+ *   splits == 0: chosen by shape (what sgemm_f32 and sgemm_f32_ex do);
+ *   splits == 1: never split;
+ *   2 <= splits <= SGEMM_MAX_SPLITS: at most that many chunks (fewer when K
+ *     has fewer slabs).
+ * Other values give SGEMM_ERR_ARG.  Shapes the matrix-core kernel cannot
+ * address (32-bit offsets) run unsplit on the 64-bit kernel.  A split result
+ * differs from the unsplit one only in the order of the additions (same
+ * error bound).  Other arguments and conventions as sgemm_f32_ex. */
+#define SGEMM_MAX_SPLITS 64
+int sgemm_f32_ex_split(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                       const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                       float *C, int64_t ldc, int splits, void *stream);
+
+/* The K split sgemm_f32_ex_split(transa, transb, M, N, K, ..., splits, ...)
+ * would run with these operands (host-only decision, no HIP call; the
+ * pointers enter only through their alignment): the number of K chunks
+ * (1 = unsplit), with the chunk length in *kchunk when kchunk is not NULL
+ * (the last chunk takes the rest of K); or minus the status code of invalid
+ * flags, sizes, leading dimensions or splits (C's leading dimension is taken
+ * as max(1, N)). */
+int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda, const float *B, int64_t ldb,
+                     int splits, int64_t *kchunk);
+
 /* The same operation in column-major storage (the BLAS and cuBLAS
  * convention): C (m x n, ldc >= max(1, m)) = alpha * op(A) op(B) + beta * C,
  * op(A) m x k, op(B) k x n; A is m x k (lda >= max(1, m)) or, transposed,

@@ -38,7 +38,10 @@ STATUS = {
 EXPORTS = ["sgemm_f32", "sgemm_f32_variant", "sgemm_copy_f32", "sgemm_copy_f32_launch",
            "sgemm_status_string", "sgemm_variant_name", "sgemm_auto_variant",
            "sgemm_last_hip_error", "sgemm_abi_version", "sgemm_probe_valu_f32",
-           "sgemm_probe_mfma_f32", "sgemm_f32_ex", "sgemm_f32_colmajor"]
+           "sgemm_probe_mfma_f32", "sgemm_f32_ex", "sgemm_f32_colmajor", "sgemm_f32_ex_split",
+           "sgemm_split_plan"]
+
+MAX_SPLITS = 64
 
 OP_N, OP_T = 0, 1
 
@@ -75,6 +78,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_f32_ex.restype = cint
     lib.sgemm_f32_colmajor.argtypes = ex
     lib.sgemm_f32_colmajor.restype = cint
+    lib.sgemm_f32_ex_split.argtypes = [*ex[:-1], cint, vp]
+    lib.sgemm_f32_ex_split.restype = cint
+    lib.sgemm_split_plan.argtypes = [cint, cint, i64, i64, i64, vp, i64, vp, i64, cint,
+                                     ctypes.POINTER(i64)]
+    lib.sgemm_split_plan.restype = cint
     lib.sgemm_copy_f32.argtypes = [vp, vp, i64, vp]
     lib.sgemm_copy_f32.restype = cint
     lib.sgemm_copy_f32_launch.argtypes = [vp, vp, i64, cint, i64, vp]
@@ -163,11 +171,13 @@ def sgemm(A, B, out=None, variant="auto"):
     return out
 
 
-def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0):
+def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0, splits=None):
     """C = alpha op(A) op(B) + beta C (row-major float32 GPU tensors).  A is
     M x K, or K x M with transa (op(A) = A^T); B is K x N, or N x K with
     transb.  ``out`` holds C (read only when beta != 0); it is allocated when
-    omitted (then beta must be 0)."""
+    omitted (then beta must be 0).  ``splits`` (sgemm_f32_ex_split): None or
+    0 chooses the K split by shape, 1 never splits, 2..64 asks for at most
+    that many K chunks."""
     import torch
     if A.device.type != "cuda" or B.device.type != "cuda":
         raise ValueError("operands must be GPU tensors")
@@ -181,12 +191,29 @@ def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0):
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     elif tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
-    st = load().sgemm_f32_ex(int(transa), int(transb), M, N, K, alpha, A.data_ptr(), _ld(A, "A"),
-                             B.data_ptr(), _ld(B, "B"), beta, out.data_ptr(), _ld(out, "out"),
-                             _stream_handle(A.device))
+    args = (int(transa), int(transb), M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(),
+            _ld(B, "B"), beta, out.data_ptr(), _ld(out, "out"))
+    if splits is None:
+        st = load().sgemm_f32_ex(*args, _stream_handle(A.device))
+    else:
+        st = load().sgemm_f32_ex_split(*args, int(splits), _stream_handle(A.device))
     if st != 0:
-        raise SgemmError(st, "sgemm_f32_ex")
+        raise SgemmError(st, "sgemm_f32_ex" if splits is None else "sgemm_f32_ex_split")
     return out
+
+
+def split_plan(M, N, K, transa=False, transb=False, lda=None, ldb=None, A_ptr=0, B_ptr=0,
+               splits=0):
+    """(chunks, kchunk) of the K split sgemm_f32_ex_split would run (host
+    only; the pointers enter only through their 16-byte alignment)."""
+    lda = (max(M, 1) if transa else max(K, 1)) if lda is None else lda
+    ldb = (max(K, 1) if transb else max(N, 1)) if ldb is None else ldb
+    kc = ctypes.c_int64(0)
+    r = load().sgemm_split_plan(int(transa), int(transb), M, N, K, A_ptr or None, lda,
+                                B_ptr or None, ldb, int(splits), ctypes.byref(kc))
+    if r < 0:
+        raise SgemmError(-r, "sgemm_split_plan")
+    return r, kc.value
 
 
 def _ld_col(t, name):

@@ -49,9 +49,10 @@ int validate(int variant, int64_t M, int64_t N, int64_t K, const float* A, int64
     return SGEMM_OK;
 }
 
-// Validation of the general entry point (row-major; see include/sgemm.h).
-int validate_ex(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
-                int64_t lda, const float* B, int64_t ldb, const float* C, int64_t ldc) {
+// Validation of the general entry point (row-major; see include/sgemm.h):
+// flags, sizes and leading dimensions, then pointers.
+int validate_ex_shape(int ta, int tb, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                      int64_t ldc) {
     if ((ta != SGEMM_OP_N && ta != SGEMM_OP_T) || (tb != SGEMM_OP_N && tb != SGEMM_OP_T))
         return SGEMM_ERR_ARG;
     if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
@@ -60,6 +61,13 @@ int validate_ex(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, co
     const int64_t m1 = M > 1 ? M : 1, n1 = N > 1 ? N : 1, k1 = K > 1 ? K : 1;
     if (lda < (ta ? m1 : k1) || ldb < (tb ? k1 : n1) || ldc < n1) return SGEMM_ERR_LD;
     if (lda > lim || ldb > lim || ldc > lim) return SGEMM_ERR_LD;
+    return SGEMM_OK;
+}
+
+int validate_ex(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                int64_t lda, const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    const int v = validate_ex_shape(ta, tb, M, N, K, lda, ldb, ldc);
+    if (v != SGEMM_OK) return v;
     if (M == 0 || N == 0) return SGEMM_OK;
     if (C == nullptr) return SGEMM_ERR_NULLPTR;
     if (K > 0 && alpha != 0.0f) {
@@ -119,9 +127,10 @@ int sgemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, cons
     return sgemm_f32_variant(SGEMM_AUTO, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
-int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
-                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
-                 int64_t ldc, void* stream) {
+int sgemm_f32_ex_split(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                       const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                       float* C, int64_t ldc, int splits, void* stream) {
+    if (splits < 0 || splits > SGEMM_MAX_SPLITS) return SGEMM_ERR_ARG;
     const int v = validate_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (v != SGEMM_OK) return v;
     if (M == 0 || N == 0) return SGEMM_OK;
@@ -132,8 +141,15 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
     g.trans_b = transb == SGEMM_OP_T;
     g.alpha = alpha;
     g.beta = beta;
-    if (sgemm::k4_supports(g)) return launch_status(sgemm::launch_k4_mfma(g, s));
+    if (sgemm::k4_supports(g)) return launch_status(sgemm::launch_k4_mfma(g, s, splits));
     return launch_status(sgemm::launch_k1_general(g, s));
+}
+
+int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                 int64_t ldc, void* stream) {
+    return sgemm_f32_ex_split(transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, 0,
+                              stream);
 }
 
 int sgemm_f32_colmajor(int transa, int transb, int64_t m, int64_t n, int64_t k, float alpha,
@@ -151,6 +167,20 @@ int sgemm_auto_variant(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     if (v != SGEMM_OK) return -v;
     const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
     return choose_auto(g);
+}
+
+int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K, const float* A,
+                     int64_t lda, const float* B, int64_t ldb, int splits, int64_t* kchunk) {
+    if (splits < 0 || splits > SGEMM_MAX_SPLITS) return -SGEMM_ERR_ARG;
+    const int v = validate_ex_shape(transa, transb, M, N, K, lda, ldb, N > 1 ? N : 1);
+    if (v != SGEMM_OK) return -v;
+    GemmArgs g{M, N, K, A, lda, B, ldb, nullptr, N > 1 ? N : 1};
+    g.trans_a = transa == SGEMM_OP_T;
+    g.trans_b = transb == SGEMM_OP_T;
+    sgemm::SplitPlan p{1, K, 0};
+    if (M > 0 && N > 0 && K > 0 && sgemm::k4_supports(g)) p = sgemm::k4_plan(g, splits);
+    if (kchunk) *kchunk = p.kchunk;
+    return p.splits;
 }
 
 int sgemm_copy_f32_launch(float* dst, const float* src, int64_t n, int block, int64_t grid,

@@ -107,11 +107,13 @@ template <class T, class F> struct pick<false, T, F> { using type = F; };
 
 // A_KMAJOR: A stored M x K (k contiguous) rather than K x M.
 // B_KMAJOR: B stored N x K (k contiguous) rather than K x N.
+// NSTAGE: LDS stages (slabs in flight); loads run NSTAGE - 1 slabs ahead.
 template <int WAVES_M_, int WAVES_N_, int TM_, int TN_, int BK_, bool VEC_, bool A_KMAJOR_ = true,
-          bool B_KMAJOR_ = false>
+          bool B_KMAJOR_ = false, int NSTAGE_ = 2>
 struct Cfg {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_, BK = BK_;
     static constexpr bool VEC = VEC_, A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_;
+    static constexpr int NSTAGE = NSTAGE_;
     static constexpr int NWAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * NWAVES;
     static constexpr int BM = WAVES_M * TM * 32, BN = WAVES_N * TN * 32;
@@ -119,11 +121,12 @@ struct Cfg {
     using LB = typename pick<B_KMAJOR, KMajor<BN, BK, VEC>, KRows<BN, BK, VEC>>::type;
     static constexpr int A_BASE = 0, B_BASE = LA::STAGE;
     static constexpr int STAGE = LA::STAGE + LB::STAGE;
-    static constexpr int LDS_BYTES = 2 * STAGE;
+    static constexpr int LDS_BYTES = NSTAGE * STAGE;
     static constexpr int A_INSTR_PER_WAVE = LA::INSTR / NWAVES;
     static constexpr int B_INSTR_PER_WAVE = LB::INSTR / NWAVES;
     static constexpr int KH = BK / 2;       // MFMA steps per slab
     static_assert(BK == 16 || BK == 32, "slab depth");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stages");
     static_assert(LA::INSTR % NWAVES == 0 && LB::INSTR % NWAVES == 0, "loads split evenly over waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 

@@ -24,6 +24,8 @@
 //    are remapped to give each XCD a contiguous range of tiles, walked in
 //    groups of GROUP_M tile-rows so that resident tiles share A and B panels
 //    in that XCD's L2.
+#include <algorithm>
+
 #include "k4_layout.h"
 #include "kernels.h"
 
@@ -50,20 +52,51 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t r, char* lds, un
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 4, off, 0, 0, 0);
 }
 
+// Wait until at most N vector-memory operations of this wave are
+// outstanding.  Loads complete in issue order, so this means every load but
+// the N most recent has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_vm<n * PER> for a run-time n in [0, MAXN].
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_vm_batches(int n) {
+    if constexpr (MAXN >= 2) {
+        if (n >= 2) { wait_vm<2 * PER>(); return; }
+    }
+    if constexpr (MAXN >= 1) {
+        if (n >= 1) { wait_vm<PER>(); return; }
+    }
+    wait_vm<0>();
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)OOB,
                                              RSRC_WORD3);
 }
 }  // namespace
 
-template <class CF, int OCC, int GM = GROUP_M, bool XCD_REMAP = true, bool SPLIT = false>
+// SPLITK: the launch has gridDim.y K-splits; split z covers k in
+// [z * kchunk, min(K, (z + 1) * kchunk)) and stores its partial product to the
+// M x N slab z of the workspace passed as C (row stride ldc).
+template <class CF, int OCC, int GM = GROUP_M, bool XCD_REMAP = true, bool SPLIT = false,
+          bool SPLITK = false>
 __global__ void __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* __restrict__ B,
         int ldb, float* __restrict__ C, int64_t ldc, float alpha, float beta, int tiles_m,
-        int tiles_n, int tiles) {
+        int tiles_n, int tiles, int kchunk) {
     // 32-bit sizes: the host routes shapes whose sizes, leading dimensions
     // or slab offsets do not fit (k4_supports) to the 64-bit kernel.
     constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH;
+    if constexpr (SPLITK) {
+        const int z = blockIdx.y, k0 = z * kchunk;
+        K = K - k0 < kchunk ? K - k0 : kchunk;
+        A += CF::A_KMAJOR ? (int64_t)k0 : (int64_t)k0 * lda;
+        B += CF::B_KMAJOR ? (int64_t)k0 : (int64_t)k0 * ldb;
+        C += (int64_t)z * M * ldc;
+    }
     using LA = typename CF::LA;
     using LB = typename CF::LB;
     __shared__ __attribute__((aligned(1024))) char smem[CF::LDS_BYTES];
@@ -140,14 +173,20 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.0f;
 
+        // Slab s lives in stage s % NS; loads run NS - 1 slabs ahead.  Every
+        // wave issues PER load instructions per slab.
+        constexpr int NS = CF::NSTAGE;
+        constexpr int PER = CF::A_INSTR_PER_WAVE + CF::B_INSTR_PER_WAVE;
+        static_assert((NS - 2) * PER <= 63, "outstanding loads fit the vmcnt field");
         const int nk = (K + CF::BK - 1) / CF::BK;
-        if (nk > 0) issue(0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int p = 0; p < NS - 1; p++)
+            if (p < nk) issue(p * CF::BK, p);
+        // Slab 0 landed: at most min(NS - 2, nk - 1) newer slabs outstanding.
+        wait_vm_batches<PER, NS - 2>(nk - 1 < NS - 2 ? nk - 1 : NS - 2);
         __syncthreads();
         for (int s = 0; s < nk; s++) {
-            const char* st = smem + (s & 1) * CF::STAGE;
-            // Lane (li, ls) supplies A[row][kslot(ls, u)] and B[kslot(ls, u)][col]
-            // for the slab's KH steps u.
+            const char* st = smem + (s % NS) * CF::STAGE;
             // Fragments are read and consumed in NH parts of KH / NH steps;
             // with NH = 2 only half of them are live at a time.
             constexpr int NH = SPLIT ? 2 : 1, KP = KH / NH;
@@ -197,10 +236,11 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             };
             float af[TM][KP], bf[TN][KP];
             read_frags(0, af, bf);
-            // The next slab's loads target the other stage; issue them once
-            // the first reads of this stage are out.
+            // The slab NS - 1 ahead goes to the stage read in the previous
+            // iteration (every wave has passed that iteration's barrier);
+            // issue its loads once the first reads of this stage are out.
             asm volatile("" ::: "memory");
-            if (s + 1 < nk) issue((s + 1) * CF::BK, int((s + 1) & 1));
+            if (s + NS - 1 < nk) issue((s + NS - 1) * CF::BK, (s + NS - 1) % NS);
             mfmas(af, bf);
 #pragma unroll
             for (int h = 1; h < NH; h++) {
@@ -215,7 +255,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             for (int mb = 0; mb < TM; mb++)
 #pragma unroll
                 for (int nb = 0; nb < TN; nb++) asm volatile("" : "+a"(acc[mb][nb]));
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // Slab s + 1 landed: the slabs after it may stay in flight.
+            const int newer = nk - 2 - s < NS - 2 ? nk - 2 - s : NS - 2;
+            wait_vm_batches<PER, NS - 2>(newer > 0 ? newer : 0);
             __syncthreads();
         }
 
@@ -256,21 +298,101 @@ hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT>), dim3(grid_for(tiles)),
                        dim3(CF::THREADS), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, g.C, g.ldc,
-                       g.alpha, g.beta, (int)tm, (int)tn, (int)tiles);
+                       g.alpha, g.beta, (int)tm, (int)tn, (int)tiles, 0);
     return hipGetLastError();
 }
 
-// The four storage orientations of (A, B) for one tile configuration.
-template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false>
-hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s) {
+// Split-K second pass: C = alpha * (sum of the S partial slabs, added in
+// split order) (+ beta * C when beta is nonzero), the same two roundings the
+// unsplit epilogue applies.  Each lane takes four consecutive columns; VEC
+// (N and ldc multiples of 4, C 16-byte aligned) moves them as one 16-byte
+// access.  W holds S dense M x N slabs.
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restrict__ C, int64_t ldc,
+              float alpha, float beta) {
+    const int nq = (N + 3) / 4;
+    const int64_t total = (int64_t)M * nq, slab = (int64_t)M * N;
+    const bool read_c = beta != 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int r = (int)(i / nq), c = (int)(i % nq) * 4;
+        const float* w = W + (int64_t)r * N + c;
+        float* cp = C + (int64_t)r * ldc + c;
+        if constexpr (VEC) {
+            v4f sum = *(const v4f*)w;
+            for (int z = 1; z < S; z++) sum += *(const v4f*)(w + z * slab);
+            v4f v;
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[e] = alpha * sum[e];
+            if (read_c) {
+                const v4f c0 = *(const v4f*)cp;
+#pragma unroll
+                for (int e = 0; e < 4; e++) v[e] = fmaf(beta, c0[e], v[e]);
+            }
+            *(v4f*)cp = v;
+        } else {
+            for (int e = 0; e < 4 && c + e < N; e++) {
+                float sum = w[e];
+                for (int z = 1; z < S; z++) sum += w[z * slab + e];
+                float v = alpha * sum;
+                if (read_c) v = fmaf(beta, cp[e], v);
+                cp[e] = v;
+            }
+        }
+    }
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, hipStream_t s) {
+    const int64_t total = g.M * ceil_div(g.N, 4);
+    const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
+    const dim3 grid(grid_for(ceil_div(total, 256)));
+    if (vec)
+        hipLaunchKernelGGL(splitk_reduce<true>, grid, dim3(256), 0, s, (int)g.M, (int)g.N, splits,
+                           ws, g.C, g.ldc, g.alpha, g.beta);
+    else
+        hipLaunchKernelGGL(splitk_reduce<false>, grid, dim3(256), 0, s, (int)g.M, (int)g.N, splits,
+                           ws, g.C, g.ldc, g.alpha, g.beta);
+    return hipGetLastError();
+}
+
+// K split into `splits` chunks of kchunk (a multiple of BK; every chunk
+// nonempty): partial products into ws (splits x M x N floats), then the
+// reduction into C.
+template <class CF, int OCC, bool SPLIT = false>
+hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
+    const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true>), dim3(grid_for(tiles), splits),
+                       dim3(CF::THREADS), 0, s,
+                       (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, ws, g.N,
+                       1.0f, 0.0f, (int)tm, (int)tn, (int)tiles, kchunk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce(g, splits, ws, s);
+}
+
+// The four storage orientations of (A, B) for one tile configuration; with
+// splits > 1 the split-K pair of launches.
+template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2>
+hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,
+                            float* ws = nullptr) {
     using k4::Cfg;
+    if (splits > 1) {
+        if (!g.trans_a && !g.trans_b)
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
+        if (!g.trans_a && g.trans_b)
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
+        if (g.trans_a && !g.trans_b)
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
+        return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
+    }
     if (!g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false>, OCC, SPLIT>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT>(g, s);
     if (!g.trans_a && g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true>, OCC, SPLIT>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT>(g, s);
     if (g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false>, OCC, SPLIT>(g, s);
-    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true>, OCC, SPLIT>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT>(g, s);
+    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT>(g, s);
 }
 
 // Largest byte offset a slab reaches from its base, per operand orientation.
@@ -316,10 +438,60 @@ hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) {
     return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s);
 }
 
-hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s) {
-    const int64_t tiles128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
-    if (vec_ok(g) && tiles128 >= 1024) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
-    return launch_k4_tile64(g, s);
+static hipError_t launch_k4_tile64_split(const GemmArgs& g, const SplitPlan& p, float* ws,
+                                         hipStream_t s) {
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s, p.splits, (int)p.kchunk, ws);
+    return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, p.splits, (int)p.kchunk, ws);
+}
+
+// Split-K (64 x 64 tiles) when the tiles alone leave the chip underused;
+// from a sweep of splits 1..32 over square 256..4096, 128^2 x 4096,
+// 256^2 x 16384 and 1024^2 x 4096:
+//  * fill: with T tiles, up to ceil(256 / T) splits (one workgroup per CU)
+//    while each keeps at least 128 of K (square 512: 1.3x; 256^2 x 16384:
+//    10.9x; 128^2 x 4096: 5.9x);
+//  * occupancy: up to 1024 / T splits (four workgroups per CU) while each
+//    keeps at least 1024 of K (1024^2 x 4096: 1.14x; square 1024, where a
+//    split would keep 512, loses 10 % and is not split);
+//  * at most 16 splits; chunks are whole slabs.
+SplitPlan k4_split_plan(const GemmArgs& g, int requested) {
+    const int64_t bk = vec_ok(g) ? 32 : 16;
+    const int64_t T = ceil_div(g.M, 64) * ceil_div(g.N, 64);
+    int64_t S = requested;
+    if (S <= 0) {
+        const int64_t fill = std::min(ceil_div(256, T), g.K / 128);
+        const int64_t occ = std::min(1024 / T, g.K / 1024);
+        S = std::min<int64_t>(std::max(fill, occ), 16);
+    }
+    S = std::min(S, ceil_div(g.K, bk));
+    if (S <= 1) return {1, g.K, 0};
+    const int64_t kc = ceil_div(ceil_div(g.K, S), bk) * bk;
+    S = ceil_div(g.K, kc);
+    return {(int)S, kc, S * g.M * g.N};
+}
+
+static bool uses_tile128(const GemmArgs& g, int requested) {
+    return requested == 0 && vec_ok(g) && ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 1024;
+}
+
+SplitPlan k4_plan(const GemmArgs& g, int requested) {
+    if (uses_tile128(g, requested)) return {1, g.K, 0};
+    return k4_split_plan(g, requested);
+}
+
+hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
+    if (uses_tile128(g, requested)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
+    const SplitPlan p = k4_split_plan(g, requested);
+    if (p.splits <= 1) return launch_k4_tile64(g, s);
+    void* ws = nullptr;
+    if (workspace_alloc(&ws, size_t(p.ws_floats) * sizeof(float), s) != hipSuccess) {
+        // No workspace: the unsplit kernel gives the same product.
+        (void)hipGetLastError();
+        return launch_k4_tile64(g, s);
+    }
+    const hipError_t e = launch_k4_tile64_split(g, p, static_cast<float*>(ws), s);
+    const hipError_t f = workspace_free(ws, s);
+    return e != hipSuccess ? e : f;
 }
 
 }  // namespace sgemm

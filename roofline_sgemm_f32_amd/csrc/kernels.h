@@ -38,7 +38,21 @@ hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k1_coalesced(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k2_lds(const GemmArgs& g, int tile, int pad, hipStream_t s);
 hipError_t launch_k3_regtile(const GemmArgs& g, hipStream_t s);
-hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s);    // tile size chosen by shape
+// Tile size and K split chosen by shape; requested_splits > 0 asks for that
+// many K chunks (at most; 1 = never split).
+hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested_splits = 0);
+// Split-K plan of the matrix-core kernel: `splits` chunks of kchunk (the last
+// one shorter) whose partial products take ws_floats floats of workspace.
+struct SplitPlan {
+    int splits;
+    int64_t kchunk, ws_floats;
+};
+SplitPlan k4_split_plan(const GemmArgs& g, int requested_splits);
+// The plan launch_k4_mfma follows (no split when it picks 128 x 128 tiles).
+SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
+// Stream-ordered scratch memory for launches that need it.
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s);
+hipError_t workspace_free(void* p, hipStream_t s);
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.

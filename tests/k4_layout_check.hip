@@ -111,6 +111,9 @@ int main() {
     CFG(1, 1, 1, 1, 16)
     CFG(2, 1, 1, 1, 16)
     CFG(1, 2, 1, 1, 16)
+    CFG(4, 2, 1, 2, 16)
+    CFG(2, 4, 2, 1, 16)
+    CFG(4, 2, 1, 2, 32)
     printf("failures: %d\n", failures);
     return failures ? 1 : 0;
 }

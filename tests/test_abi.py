@@ -165,3 +165,67 @@ def test_colmajor_maps_to_swapped_rowmajor(lib):
     assert f(1, 0, 4, 5, 6, 1.0, PA, 5, PB, 6, 0.0, PC, 4, None) == LD   # A k x m: lda >= k
     assert f(0, 1, 4, 5, 6, 1.0, PA, 4, PB, 4, 0.0, PC, 4, None) == LD   # B n x k: ldb >= n
     assert f(3, 0, 4, 5, 6, 1.0, PA, 4, PB, 6, 0.0, PC, 4, None) == ARG
+
+
+def test_ex_split_validation(lib):
+    f = rs.load().sgemm_f32_ex_split
+    # The split request is checked first; the rest as sgemm_f32_ex.
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 6, PB, 5, 0.0, PC, 5, -1, None) == ARG
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 6, PB, 5, 0.0, PC, 5, rs.MAX_SPLITS + 1, None) == ARG
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 5, PB, 5, 0.0, PC, 5, 2, None) == LD
+    assert f(0, 0, -1, 5, 6, 1.0, PA, 6, PB, 5, 0.0, PC, 5, 2, None) == DIM
+    assert f(0, 0, 4, 5, 6, 1.0, PA, 6, PB, 5, 0.0, PA + 4, 5, 2, None) == ALIAS
+    assert f(2, 0, 4, 5, 6, 1.0, PA, 6, PB, 5, 0.0, PC, 5, 2, None) == ARG
+    assert f(0, 0, 0, 5, 6, 1.0, None, 6, None, 5, 0.0, None, 5, rs.MAX_SPLITS, None) == OK
+
+
+def test_split_plan_errors(lib):
+    with pytest.raises(rs.SgemmError):
+        rs.split_plan(64, 64, 64, splits=-1)
+    with pytest.raises(rs.SgemmError):
+        rs.split_plan(64, 64, 64, lda=10)
+    with pytest.raises(rs.SgemmError):
+        rs.split_plan(-1, 64, 64)
+
+
+ALIGNED = 1 << 40  # a 16-byte aligned fake address
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 512, 512), (1024, 1024, 1024),
+                                   (1024, 1024, 4096), (256, 256, 16384), (128, 128, 4096),
+                                   (2048, 2048, 2048), (4096, 4096, 4096), (1, 1, 1),
+                                   (300, 17, 129), (3001, 4099, 2047), (64, 64, 1 << 20)])
+@pytest.mark.parametrize("trans", [(0, 0), (1, 1)])
+def test_split_plan_chunks_cover_k(lib, M, N, K, trans):
+    # Whatever is asked, the chunks are whole slabs (32 of K with 16-byte
+    # loads, else 16), every chunk is nonempty and together they cover K once.
+    for splits in [0, 1, 2, 3, 5, 16, rs.MAX_SPLITS]:
+        for ptr in [ALIGNED, ALIGNED + 4]:
+            S, kc = rs.split_plan(M, N, K, transa=trans[0], transb=trans[1], A_ptr=ptr,
+                                  B_ptr=ALIGNED, splits=splits)
+            assert S >= 1
+            if S == 1:
+                assert kc == K
+                continue
+            vec = ptr % 16 == 0 and (M if trans[0] else K) % 4 == 0 and (K if trans[1] else N) % 4 == 0
+            assert kc % (32 if vec else 16) == 0
+            assert (S - 1) * kc < K <= S * kc
+            assert S <= (16 if splits == 0 else splits)
+            if splits == 1:
+                raise AssertionError("splits=1 must not split")
+
+
+def test_split_plan_choices(lib):
+    # Shapes whose 64 x 64 tiles underfill the chip are split; square
+    # 1024 .. 4096 are not (measured: a split loses there).
+    plan = lambda M, N, K: rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)[0]
+    assert plan(256, 256, 16384) == 16
+    assert plan(128, 128, 4096) == 16
+    assert plan(512, 512, 512) == 4
+    assert plan(1024, 1024, 4096) == 4
+    assert plan(256, 256, 256) == 2
+    for n in (1024, 2048, 4096, 8192):
+        assert plan(n, n, n) == 1
+    assert plan(3001, 4099, 2047) == 1
+    # A short K is never cut below one slab.
+    assert plan(64, 64, 40) == 1
