@@ -67,29 +67,51 @@ def read_traffic(kernel: str, workload: str):
     return int(rec["bytes_per_launch"]) if "bytes_per_launch" in rec else None
 
 
-def time_launches(fn, steps: int, warmup: int):
+def time_launches(fn, steps: int, warmup: int, per_launch: bool = True):
     """Warm up, then time ``steps`` back-to-back launches on the current
     stream; returns (mean ms per step, mean ms per launch from per-launch
-    event pairs)."""
+    event pairs, or None without them)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    n = steps if per_launch else 0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
-    for i in range(steps):
-        starts[i].record()
-        fn()
-        ends[i].record()
+    if per_launch:
+        for i in range(steps):
+            starts[i].record()
+            fn()
+            ends[i].record()
+    else:
+        for _ in range(steps):
+            fn()
     t1.record()
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1) / steps
-    per = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    per = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps if per_launch else None
     return total, per
+
+
+def launch_times(fn, steps: int, warmup: int):
+    """Per-launch durations (ms) of ``steps`` back-to-back launches, each
+    between its own pair of events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
 
 
 def run_gemm_factory(variant, A, B, C):
@@ -202,24 +224,30 @@ def copy_probe(steps: int, block=None, grid=None):
             "block": block or 64, "grid": grid}
 
 
-def compute_probe(valu_iters=4096, mfma_iters=2048):
+def compute_probe(valu_iters=4096, mfma_iters=2048, steps=20, warmup=5):
     """Sustained FP32 rate of register-only multiply-add chains (vector ALU)
-    and of back-to-back FP32 matrix instructions, for the compute roof."""
+    and of back-to-back FP32 matrix instructions, for the compute roof: mean
+    over the timed launches, and the fastest launch (the chip's clock, and so
+    these rates, drop when it runs into its power limit)."""
+    import statistics
     import torch
     import roofline_sgemm_f32_amd as rs
     from roofline_sgemm_f32_amd.inputs import probe_operands
     blocks, block = 256 * 8, 256  # 32 waves per CU
     out_v = torch.empty((blocks * block, 16), device="cuda")
-    _, per_v = time_launches(lambda: rs.probe_valu(blocks, block, valu_iters, 0.999, 0.001, out_v), 5, 1)
-    valu_tf = blocks * block * valu_iters * 16 * 2 / (per_v * 1e-3) / 1e12
+    tv = launch_times(lambda: rs.probe_valu(blocks, block, valu_iters, 0.999, 0.001, out_v), steps, warmup)
+    fv = blocks * block * valu_iters * 16 * 2
     a, b = probe_operands(7)
     a, b = a.cuda(), b.cuda()
     mblocks = 256 * 4  # 16 waves per CU
     out_m = torch.empty((mblocks * 4, 4, 32, 32), device="cuda")
-    _, per_m = time_launches(lambda: rs.probe_mfma(a, b, mblocks, mfma_iters, out_m), 5, 1)
-    mfma_tf = mblocks * 16 * mfma_iters * 4096 / (per_m * 1e-3) / 1e12
-    return {"valu_fma_tflops": round(valu_tf, 2), "mfma_f32_tflops": round(mfma_tf, 2),
-            "valu_ms": round(per_v, 4), "mfma_ms": round(per_m, 4)}
+    tm = launch_times(lambda: rs.probe_mfma(a, b, mblocks, mfma_iters, out_m), steps, warmup)
+    fm = mblocks * 16 * mfma_iters * 4096
+    tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 2)
+    return {"valu_fma_tflops": tf(fv, statistics.mean(tv)), "valu_fma_tflops_best": tf(fv, min(tv)),
+            "mfma_f32_tflops": tf(fm, statistics.mean(tm)), "mfma_f32_tflops_best": tf(fm, min(tm)),
+            "valu_ms": round(statistics.mean(tv), 4), "mfma_ms": round(statistics.mean(tm), 4),
+            "launches": steps}
 
 
 def ladder(args, out):
@@ -263,6 +291,75 @@ def ladder(args, out):
     return rows
 
 
+# Small-shape path: shapes whose 64 x 64 tiles underfill the 256 compute
+# units (the two small workloads plus K-heavy outputs), timed with the K
+# split the library chooses and unsplit.
+SMALL_SHAPES = {
+    "square256": None,
+    "square512": (512, 512, 512),
+    "square1024": None,
+    "kheavy128x128x4096": (128, 128, 4096),
+    "kheavy256x256x16384": (256, 256, 16384),
+    "kheavy1024x1024x4096": (1024, 1024, 4096),
+}
+
+
+def small_shapes(reps: int, only=None):
+    """Per shape: chunks chosen, us per call split (as chosen) and unsplit:
+    back-to-back calls on one stream, so a call's time is the larger of its
+    device time and its host launch cost."""
+    import torch
+    import roofline_sgemm_f32_amd as rs
+    from roofline_sgemm_f32_amd import metrics as m
+    from roofline_sgemm_f32_amd.inputs import WORKLOADS, make_operands
+    lib = rs.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for name, dims in SMALL_SHAPES.items():
+        if only and name not in only:
+            continue
+        if dims is None:
+            w = WORKLOADS[name]
+            _, _, A, B, C = device_operands(w)
+        else:
+            M, N, K = dims
+            A_h, B_h = make_operands(M, N, K, "uniform", seed=100 + len(rows))
+            A, B = A_h.cuda(), B_h.cuda()
+            C = torch.full((M, N), float("nan"), device="cuda")
+        M, K = A.shape
+        N = B.shape[1]
+        args = (M, N, K, 1.0, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), 0.0,
+                C.data_ptr(), C.stride(0))
+        chunks, kchunk = rs.split_plan(M, N, K, lda=A.stride(0), ldb=B.stride(0),
+                                       A_ptr=A.data_ptr(), B_ptr=B.data_ptr())
+
+        def call(splits):
+            def fn():
+                st = lib.sgemm_f32_ex_split(0, 0, *args, splits, stream)
+                if st != 0:
+                    raise rs.SgemmError(st, "sgemm_f32_ex_split")
+            return fn
+        flops = m.sgemm_flops(M, N, K)
+        # Warm up for about 50 ms per plan (the clock settles over tens of ms).
+        t0 = time.perf_counter()
+        call(1)()
+        torch.cuda.synchronize()
+        warm = int(min(5000, max(20, 0.05 / max(time.perf_counter() - t0, 1e-6))))
+        t_auto, _ = time_launches(call(0), reps, warm, per_launch=False)
+        t_one, _ = time_launches(call(1), reps, warm, per_launch=False)
+        rec = {"shape": name, "M": M, "N": N, "K": K, "chunks": chunks, "kchunk": kchunk,
+               "us_per_call": round(1e3 * t_auto, 2), "gflops": round(m.gflops(flops, t_auto), 1),
+               "unsplit_us_per_call": round(1e3 * t_one, 2),
+               "unsplit_gflops": round(m.gflops(flops, t_one), 1),
+               "speedup_vs_unsplit": round(t_one / t_auto, 3)}
+        rows.append(rec)
+        log(f"  small {name:22s} chunks={chunks:2d} {rec['us_per_call']:9.2f} us "
+            f"{rec['gflops']:9.1f} GFLOP/s (unsplit {rec['unsplit_us_per_call']:9.2f} us) "
+            f"x{rec['speedup_vs_unsplit']}")
+        del A, B, C
+    return rows
+
+
 def main():
     from roofline_sgemm_f32_amd.inputs import WORKLOADS
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -281,6 +378,10 @@ def main():
     p.add_argument("--ladder-workloads", default="square4096")
     p.add_argument("--ladder-reps", type=int, default=20)
     p.add_argument("--out", default=None, help="append extra JSON lines (ladder, sweep) here")
+    p.add_argument("--small-reps", type=int, default=200,
+                   help="calls timed per small shape (0 skips the small-shape section)")
+    p.add_argument("--small-only", default=None,
+                   help="comma-separated small shapes: time only these and print their JSON")
     args = p.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -298,6 +399,10 @@ def main():
         sys.exit(1)
     rs.load()  # raises when the HIP library is missing: no fallback
     out = open(args.out, "a") if args.out else None
+    if args.small_only:
+        print(json.dumps({"small_shapes": small_shapes(max(args.small_reps, 1),
+                                                       args.small_only.split(","))}), flush=True)
+        return
 
     w = WORKLOADS[args.workload]
     A_h, B_h, A, B, C = device_operands(w)
@@ -328,8 +433,9 @@ def main():
         log(f"[bench] copy probe {copy['gbs']} GB/s ({100 * copy['frac']:.1f}% of 8 TB/s)")
     probe = compute_probe() if args.compute_probe else None
     if probe:
-        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s, "
-            f"FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s")
+        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s "
+            f"(best {probe['valu_fma_tflops_best']}), FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s "
+            f"(best {probe['mfma_f32_tflops_best']})")
     if args.copy_sweep:
         from roofline_sgemm_f32_amd.inputs import COPY_ELEMENTS  # noqa: F401
         for block in (64, 128, 256, 512, 1024):
@@ -340,6 +446,7 @@ def main():
                     out.write(json.dumps({"copy_sweep": r}) + "\n")
     if args.ladder:
         ladder(args, out)
+    small = small_shapes(args.small_reps) if args.small_reps > 0 else None
 
     traffic = read_traffic(resolved, w.name)
     kernel = resolved
@@ -368,6 +475,7 @@ def main():
         "gate": gate,
         "hbm_copy": copy,
         "compute_probe": probe,
+        "small_shapes": small,
     }
     if out:
         out.write(json.dumps({"bench": line}) + "\n")

@@ -119,10 +119,13 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
  * Split-K cuts K into chunks of whole slabs that run as separate workgroups;
  * each stores its partial product to a workspace of (chunks x M x N) floats,
  * and a second kernel adds the partials in chunk order and applies alpha and
- * beta.  The workspace is allocated stream-ordered on `stream` from a memory
- * pool the library keeps per device (up to 256 MiB stays reserved between
- * calls) and released on `stream` after the second kernel; if it cannot be
- * allocated the product runs unsplit.
+ * beta.  The workspace is library memory: one buffer per device, allocated
+ * stream-ordered (from a memory pool the library creates) on first need,
+ * grown on demand up to 256 MiB and kept for later calls; a larger request
+ * gets a buffer of its own, freed stream-ordered after the call.  Split calls
+ * on one device take the buffer in turn (a host lock around their launches;
+ * a call on another stream than the previous one waits for it on the GPU).
+ * If the workspace cannot be allocated the product runs unsplit.
  *   splits == 0: chosen by shape (what sgemm_f32 and sgemm_f32_ex do);
  *   splits == 1: never split;
  *   2 <= splits <= SGEMM_MAX_SPLITS: at most that many chunks (fewer when K

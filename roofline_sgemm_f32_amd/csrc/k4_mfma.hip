@@ -444,24 +444,23 @@ static hipError_t launch_k4_tile64_split(const GemmArgs& g, const SplitPlan& p, 
     return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, p.splits, (int)p.kchunk, ws);
 }
 
-// Split-K (64 x 64 tiles) when the tiles alone leave the chip underused;
-// from a sweep of splits 1..32 over square 256..4096, 128^2 x 4096,
-// 256^2 x 16384 and 1024^2 x 4096:
-//  * fill: with T tiles, up to ceil(256 / T) splits (one workgroup per CU)
-//    while each keeps at least 128 of K (square 512: 1.3x; 256^2 x 16384:
-//    10.9x; 128^2 x 4096: 5.9x);
-//  * occupancy: up to 1024 / T splits (four workgroups per CU) while each
-//    keeps at least 1024 of K (1024^2 x 4096: 1.14x; square 1024, where a
-//    split would keep 512, loses 10 % and is not split);
-//  * at most 16 splits; chunks are whole slabs.
+// Split-K (64 x 64 tiles) when the tiles alone leave the chip underused.
+// From a sweep of splits 1..32 over square 256..4096, 128^2 x 4096,
+// 256^2 x 16384 and 1024^2 x 4096, timed as back-to-back calls (so the
+// second launch, about 2.5 us, counts): with T tiles, up to ceil(256 / T)
+// splits (one workgroup per CU), each keeping at least 256 of K, and only
+// when a workgroup's share of K shrinks by at least 512 (256^2 x 16384:
+// 9.4x; 128^2 x 4096: 5x).  Smaller savings do not pay for the second launch
+// and the partial sums' traffic (square 256 and 512 measured within noise or
+// slower), nor did more splits once every CU has a workgroup (1024^2 x 4096:
+// 0.96x..1.05x over runs).  At most 16 splits; chunks are whole slabs.
 SplitPlan k4_split_plan(const GemmArgs& g, int requested) {
     const int64_t bk = vec_ok(g) ? 32 : 16;
     const int64_t T = ceil_div(g.M, 64) * ceil_div(g.N, 64);
     int64_t S = requested;
     if (S <= 0) {
-        const int64_t fill = std::min(ceil_div(256, T), g.K / 128);
-        const int64_t occ = std::min(1024 / T, g.K / 1024);
-        S = std::min<int64_t>(std::max(fill, occ), 16);
+        S = std::min<int64_t>(std::min(ceil_div(256, T), g.K / 256), 16);
+        if (S >= 2 && g.K - ceil_div(g.K, S) < 512) S = 1;
     }
     S = std::min(S, ceil_div(g.K, bk));
     if (S <= 1) return {1, g.K, 0};
@@ -483,14 +482,14 @@ hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
     if (uses_tile128(g, requested)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
     const SplitPlan p = k4_split_plan(g, requested);
     if (p.splits <= 1) return launch_k4_tile64(g, s);
-    void* ws = nullptr;
-    if (workspace_alloc(&ws, size_t(p.ws_floats) * sizeof(float), s) != hipSuccess) {
+    Workspace ws;
+    if (workspace_acquire(size_t(p.ws_floats) * sizeof(float), s, &ws) != hipSuccess) {
         // No workspace: the unsplit kernel gives the same product.
         (void)hipGetLastError();
         return launch_k4_tile64(g, s);
     }
-    const hipError_t e = launch_k4_tile64_split(g, p, static_cast<float*>(ws), s);
-    const hipError_t f = workspace_free(ws, s);
+    const hipError_t e = launch_k4_tile64_split(g, p, static_cast<float*>(ws.ptr), s);
+    const hipError_t f = workspace_release(&ws, s);
     return e != hipSuccess ? e : f;
 }
 

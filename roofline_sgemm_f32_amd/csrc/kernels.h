@@ -4,6 +4,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <mutex>
 
 namespace sgemm {
 
@@ -50,9 +51,17 @@ struct SplitPlan {
 SplitPlan k4_split_plan(const GemmArgs& g, int requested_splits);
 // The plan launch_k4_mfma follows (no split when it picks 128 x 128 tiles).
 SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
-// Stream-ordered scratch memory for launches that need it.
-hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s);
-hipError_t workspace_free(void* p, hipStream_t s);
+// Scratch memory for launches that need it: the device's cached buffer,
+// held (with the device's workspace lock) from acquire to release; every
+// launch that uses it goes on stream s in between.
+struct Workspace {
+    void* ptr = nullptr;
+    bool own = false;  // a one-off buffer, freed stream-ordered on release
+    int dev = 0;
+    std::unique_lock<std::mutex> lock;
+};
+hipError_t workspace_acquire(size_t bytes, hipStream_t s, Workspace* ws);
+hipError_t workspace_release(Workspace* ws, hipStream_t s);
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.

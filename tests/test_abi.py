@@ -221,9 +221,13 @@ def test_split_plan_choices(lib):
     plan = lambda M, N, K: rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)[0]
     assert plan(256, 256, 16384) == 16
     assert plan(128, 128, 4096) == 16
-    assert plan(512, 512, 512) == 4
-    assert plan(1024, 1024, 4096) == 4
-    assert plan(256, 256, 256) == 2
+    assert plan(256, 256, 2048) == 8
+    assert plan(128, 128, 1024) == 4
+    assert plan(256, 256, 768) == 3
+    # Too little K to save: square 256 and 512; every CU already busy: 1024^2 x 4096.
+    assert plan(256, 256, 256) == 1
+    assert plan(512, 512, 512) == 1
+    assert plan(1024, 1024, 4096) == 1
     for n in (1024, 2048, 4096, 8192):
         assert plan(n, n, n) == 1
     assert plan(3001, 4099, 2047) == 1

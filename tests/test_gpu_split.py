@@ -120,8 +120,8 @@ def test_split_one_is_the_unsplit_kernel():
 
 # Shapes the shape-chosen plan splits, at full size through the plain entry
 # point sgemm_f32 (AUTO): every element against the oracle.
-AUTO_SPLIT = [(256, 256, 256, 2), (512, 512, 512, 4), (128, 128, 4096, 16), (256, 256, 16384, 16),
-              (1024, 1024, 4096, 4), (200, 120, 3000, 0)]
+AUTO_SPLIT = [(256, 256, 768, 3), (128, 128, 1024, 4), (128, 128, 4096, 16), (256, 256, 16384, 16),
+              (256, 256, 2048, 8), (200, 120, 3000, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,want", AUTO_SPLIT, ids=lambda v: str(v))
