@@ -177,7 +177,7 @@ int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K, co
     GemmArgs g{M, N, K, A, lda, B, ldb, nullptr, N > 1 ? N : 1};
     g.trans_a = transa == SGEMM_OP_T;
     g.trans_b = transb == SGEMM_OP_T;
-    sgemm::SplitPlan p{1, K, 0};
+    sgemm::SplitPlan p{1, K, 0, 0};
     if (M > 0 && N > 0 && K > 0 && sgemm::k4_supports(g)) p = sgemm::k4_plan(g, splits);
     if (kchunk) *kchunk = p.kchunk;
     return p.splits;

@@ -81,15 +81,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 // SPLITK: the launch has gridDim.y K-splits; split z covers k in
 // [z * kchunk, min(K, (z + 1) * kchunk)) and stores its partial product to the
 // M x N slab z of the workspace passed as C (row stride ldc).
+// WK: the workgroup holds WK groups of CF's waves over the same tile; group g
+// takes slabs g, g + WK, g + 2 WK, ... in LDS stages of its own, and the
+// groups' accumulators are added through LDS (group order) before group 0
+// stores the tile.  This shortens each wave's chain of dependent MFMAs by
+// WK without scratch memory or a second launch.
 template <class CF, int OCC, int GM = GROUP_M, bool XCD_REMAP = true, bool SPLIT = false,
-          bool SPLITK = false>
-__global__ void __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+          bool SPLITK = false, int WK = 1>
+__global__ void __launch_bounds__(CF::THREADS * WK) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* __restrict__ B,
         int ldb, float* __restrict__ C, int64_t ldc, float alpha, float beta, int tiles_m,
         int tiles_n, int tiles, int kchunk) {
     // 32-bit sizes: the host routes shapes whose sizes, leading dimensions
     // or slab offsets do not fit (k4_supports) to the 64-bit kernel.
     constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH;
+    constexpr int WG_WAVES = CF::NWAVES;  // waves of one K group
+    // Partial accumulators of groups 1.. WK-1, one float per lane and register.
+    constexpr int RED_BYTES = (WK - 1) * WG_WAVES * TM * TN * 16 * 64 * 4;
+    constexpr int LDS_TOTAL = CF::LDS_BYTES * WK > RED_BYTES ? CF::LDS_BYTES * WK : RED_BYTES;
+    static_assert(WK >= 1 && WK <= 8 && CF::THREADS * WK <= 1024, "K groups");
+    static_assert(LDS_TOTAL <= 160 * 1024, "LDS per workgroup");
     if constexpr (SPLITK) {
         const int z = blockIdx.y, k0 = z * kchunk;
         K = K - k0 < kchunk ? K - k0 : kchunk;
@@ -99,9 +110,11 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     }
     using LA = typename CF::LA;
     using LB = typename CF::LB;
-    __shared__ __attribute__((aligned(1024))) char smem[CF::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = WK > 1 ? wave_all / WG_WAVES : 0;       // K group
+    const int wave = WK > 1 ? wave_all % WG_WAVES : wave_all;  // wave within the group
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
     const int li = lane & 31, ls = lane >> 5;
 
@@ -120,7 +133,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         const int col0 = ((lin % per_group) / gsz) * CF::BN;
 
         auto issue = [&](int k0, int stage) {
-            char* base = smem + stage * CF::STAGE;
+            char* base = smem + (stage * WK + kg) * CF::STAGE;
             if constexpr (CF::A_KMAJOR) {  // A stored M x K
                 const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * lda + k0);
 #pragma unroll
@@ -173,20 +186,26 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.0f;
 
-        // Slab s lives in stage s % NS; loads run NS - 1 slabs ahead.  Every
-        // wave issues PER load instructions per slab.
+        // The group's s-th slab (K slab s * WK + kg) lives in stage s % NS;
+        // loads run NS - 1 slabs ahead.  Every wave issues PER load
+        // instructions per slab of its group.
         constexpr int NS = CF::NSTAGE;
         constexpr int PER = CF::A_INSTR_PER_WAVE + CF::B_INSTR_PER_WAVE;
         static_assert((NS - 2) * PER <= 63, "outstanding loads fit the vmcnt field");
-        const int nk = (K + CF::BK - 1) / CF::BK;
+        const int nk_all = (K + CF::BK - 1) / CF::BK;
+        const int iters = (nk_all + WK - 1) / WK;                       // group 0's slab count
+        const int nk = kg < nk_all ? (nk_all - kg + WK - 1) / WK : 0;   // this group's
 #pragma unroll
         for (int p = 0; p < NS - 1; p++)
-            if (p < nk) issue(p * CF::BK, p);
+            if (p < nk) issue((p * WK + kg) * CF::BK, p);
         // Slab 0 landed: at most min(NS - 2, nk - 1) newer slabs outstanding.
-        wait_vm_batches<PER, NS - 2>(nk - 1 < NS - 2 ? nk - 1 : NS - 2);
+        {
+            const int newer = nk - 1 < NS - 2 ? nk - 1 : NS - 2;
+            wait_vm_batches<PER, NS - 2>(newer > 0 ? newer : 0);
+        }
         __syncthreads();
-        for (int s = 0; s < nk; s++) {
-            const char* st = smem + (s % NS) * CF::STAGE;
+        for (int s = 0; s < iters; s++) {
+            const char* st = smem + ((s % NS) * WK + kg) * CF::STAGE;
             // Fragments are read and consumed in NH parts of KH / NH steps;
             // with NH = 2 only half of them are live at a time.
             constexpr int NH = SPLIT ? 2 : 1, KP = KH / NH;
@@ -234,19 +253,22 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb][u], bf[nb][u],
                                                                                acc[mb][nb], 0, 0, 0);
             };
-            float af[TM][KP], bf[TN][KP];
-            read_frags(0, af, bf);
-            // The slab NS - 1 ahead goes to the stage read in the previous
-            // iteration (every wave has passed that iteration's barrier);
-            // issue its loads once the first reads of this stage are out.
-            asm volatile("" ::: "memory");
-            if (s + NS - 1 < nk) issue((s + NS - 1) * CF::BK, (s + NS - 1) % NS);
-            mfmas(af, bf);
-#pragma unroll
-            for (int h = 1; h < NH; h++) {
-                __builtin_amdgcn_sched_barrier(0);
-                read_frags(h, af, bf);
+            if (WK == 1 || s < nk) {
+                float af[TM][KP], bf[TN][KP];
+                read_frags(0, af, bf);
+                // The slab NS - 1 ahead goes to the stage read in the
+                // previous iteration (every wave has passed that iteration's
+                // barrier); issue its loads once the first reads of this
+                // stage are out.
+                asm volatile("" ::: "memory");
+                if (s + NS - 1 < nk) issue(((s + NS - 1) * WK + kg) * CF::BK, (s + NS - 1) % NS);
                 mfmas(af, bf);
+#pragma unroll
+                for (int h = 1; h < NH; h++) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_frags(h, af, bf);
+                    mfmas(af, bf);
+                }
             }
             // Register-only MFMAs may otherwise be scheduled after the wait
             // and barrier below, which would expose the load latency; tie
@@ -259,6 +281,36 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             const int newer = nk - 2 - s < NS - 2 ? nk - 2 - s : NS - 2;
             wait_vm_batches<PER, NS - 2>(newer > 0 ? newer : 0);
             __syncthreads();
+        }
+
+        if constexpr (WK > 1) {
+            // Every stage is free after the loop's last barrier: groups
+            // 1 .. WK-1 leave their accumulators there, group 0 adds them in
+            // group order.
+            float* red = reinterpret_cast<float*>(smem);
+            auto slot = [&](int g, int mb, int nb, int r) {
+                return ((((g - 1) * WG_WAVES + wave) * TM + mb) * TN * 16 + nb * 16 + r) * 64 + lane;
+            };
+            if (kg > 0) {
+#pragma unroll
+                for (int mb = 0; mb < TM; mb++)
+#pragma unroll
+                    for (int nb = 0; nb < TN; nb++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++) red[slot(kg, mb, nb, r)] = acc[mb][nb][r];
+            }
+            __syncthreads();
+            if (kg == 0) {
+                for (int g = 1; g < WK; g++)
+#pragma unroll
+                    for (int mb = 0; mb < TM; mb++)
+#pragma unroll
+                        for (int nb = 0; nb < TN; nb++)
+#pragma unroll
+                            for (int r = 0; r < 16; r++) acc[mb][nb][r] += red[slot(g, mb, nb, r)];
+            }
+            __syncthreads();  // the next tile's loads reuse this memory
+            if (kg > 0) continue;
         }
 
         // Accumulator register r of lane L holds row 8*(r/4) + 4*(L/32) + r%4,
@@ -292,11 +344,11 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     }
 }
 
-template <class CF, int OCC, bool SPLIT = false>
+template <class CF, int OCC, bool SPLIT = false, int WK = 1>
 hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
-    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT>), dim3(grid_for(tiles)),
-                       dim3(CF::THREADS), 0, s,
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, false, WK>), dim3(grid_for(tiles)),
+                       dim3(CF::THREADS * WK), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, g.C, g.ldc,
                        g.alpha, g.beta, (int)tm, (int)tn, (int)tiles, 0);
     return hipGetLastError();
@@ -359,11 +411,11 @@ hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, 
 // K split into `splits` chunks of kchunk (a multiple of BK; every chunk
 // nonempty): partial products into ws (splits x M x N floats), then the
 // reduction into C.
-template <class CF, int OCC, bool SPLIT = false>
+template <class CF, int OCC, bool SPLIT = false, int WK = 1>
 hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
-    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true>), dim3(grid_for(tiles), splits),
-                       dim3(CF::THREADS), 0, s,
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true, WK>), dim3(grid_for(tiles), splits),
+                       dim3(CF::THREADS * WK), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, ws, g.N,
                        1.0f, 0.0f, (int)tm, (int)tn, (int)tiles, kchunk);
     const hipError_t e = hipGetLastError();
@@ -372,27 +424,30 @@ hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float
 }
 
 // The four storage orientations of (A, B) for one tile configuration; with
-// splits > 1 the split-K pair of launches.
-template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2>
+// splits > 1 (and CAN_SPLIT) the split-K pair of launches.
+template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2,
+          int WK = 1, bool CAN_SPLIT = true>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,
                             float* ws = nullptr) {
     using k4::Cfg;
-    if (splits > 1) {
-        if (!g.trans_a && !g.trans_b)
-            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
-        if (!g.trans_a && g.trans_b)
-            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
-        if (g.trans_a && !g.trans_b)
-            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
-        return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT>(g, splits, kchunk, ws, s);
+    if constexpr (CAN_SPLIT) {
+        if (splits > 1) {
+            if (!g.trans_a && !g.trans_b)
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
+            if (!g.trans_a && g.trans_b)
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
+            if (g.trans_a && !g.trans_b)
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
+        }
     }
     if (!g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT, WK>(g, s);
     if (!g.trans_a && g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT, WK>(g, s);
     if (g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT>(g, s);
-    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT, WK>(g, s);
+    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT, WK>(g, s);
 }
 
 // Largest byte offset a slab reaches from its base, per operand orientation.
@@ -419,76 +474,121 @@ static bool vec_ok(const GemmArgs& g) {
            a_run % 4 == 0 && b_run % 4 == 0;
 }
 
-// Tile configurations (chosen from a sweep over square 256..8192, skinny and
-// unaligned shapes on MI355X):
-//  * 128 x 128 tiles, 4 waves of 2 x 2 accumulators, K slabs of 16, 4 waves
-//    per SIMD: best once there are at least 1024 tiles (4 per CU), e.g.
-//    square 4096 and 8192;
-//  * 64 x 64 tiles, 4 waves of 1 accumulator: below that, the larger tile
-//    count fills the 256 CUs (square 1024: 2.9x faster than 128 x 128);
-//    K slabs of 32 with 16-byte loads (fragments read in two halves: another
-//    7 % on square 1024), of 16 with 4-byte loads.
+// Tile configurations, chosen from sweeps on MI355X (square 256..8192,
+// K-heavy 64^2 x 65536 .. 1024^2 x 4096, skinny and unaligned shapes; every
+// sweep row checked bit-exact against a reference on integer data):
+//  * T128: 128 x 128 tiles, 4 waves of 2 x 2 accumulators, K slabs of 16,
+//    4 waves per SIMD: best once there are at least 1024 tiles (4 per CU),
+//    e.g. square 4096 and 8192;
+//  * T64: 64 x 64 tiles, 4 waves of 1 accumulator, K slabs of 32 with
+//    16-byte loads (fragments read in two halves: 7 % on square 1024), of 16
+//    with 4-byte loads: from 512 tiles up (2048^2, 3001 x 4099 x 2047);
+//  * T64_WK4: the same tile with 4 K groups (16 waves): below 512 such tiles
+//    with 16-byte loads (square 1024: 24.1 us against 25.1; 1024^2 x 4096:
+//    79.8 against 86.9);
+//  * T32_WK4: 32 x 32 tiles, one wave per K group, 4 groups: outputs of at
+//    most 256 such tiles (square 256: 5.0 us against 7.9; square 512: 6.9
+//    against 13.2), and with 4-byte loads below 512 tiles of 64 x 64 as well
+//    (1024 x 1027 x 1024: 41.5 against 52.0).  A wave's chain of dependent
+//    matrix instructions is what bounds these shapes: 32 x 32 tiles give more
+//    workgroups, K groups shorten each chain.
+enum K4Cfg { K4_T128, K4_T64, K4_T64_WK4, K4_T32_WK4 };
+
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
-    return launch_k4_orient<2, 2, 2, 2, 16, false, 3>(g, s);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4, false, 2, 1, false>(g, s);
+    return launch_k4_orient<2, 2, 2, 2, 16, false, 3, false, 2, 1, false>(g, s);
 }
 
-hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s);
-    return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s);
+static hipError_t launch_k4_t64(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws) {
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s, splits, kchunk, ws);
+    return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, splits, kchunk, ws);
 }
 
-static hipError_t launch_k4_tile64_split(const GemmArgs& g, const SplitPlan& p, float* ws,
-                                         hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s, p.splits, (int)p.kchunk, ws);
-    return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, p.splits, (int)p.kchunk, ws);
+hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) { return launch_k4_t64(g, s, 1, 0, nullptr); }
+
+static hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
+                                    float* ws) {
+    if (vec_ok(g)) return launch_k4_orient<1, 1, 1, 1, 32, true, 4, true, 2, 4>(g, s, splits, kchunk, ws);
+    return launch_k4_orient<1, 1, 1, 1, 16, false, 8, false, 2, 4>(g, s, splits, kchunk, ws);
 }
 
-// Split-K (64 x 64 tiles) when the tiles alone leave the chip underused.
-// From a sweep of splits 1..32 over square 256..4096, 128^2 x 4096,
-// 256^2 x 16384 and 1024^2 x 4096, timed as back-to-back calls (so the
-// second launch, about 2.5 us, counts): with T tiles, up to ceil(256 / T)
-// splits (one workgroup per CU), each keeping at least 256 of K, and only
-// when a workgroup's share of K shrinks by at least 512 (256^2 x 16384:
-// 9.4x; 128^2 x 4096: 5x).  Smaller savings do not pay for the second launch
-// and the partial sums' traffic (square 256 and 512 measured within noise or
-// slower), nor did more splits once every CU has a workgroup (1024^2 x 4096:
-// 0.96x..1.05x over runs).  At most 16 splits; chunks are whole slabs.
-SplitPlan k4_split_plan(const GemmArgs& g, int requested) {
-    const int64_t bk = vec_ok(g) ? 32 : 16;
-    const int64_t T = ceil_div(g.M, 64) * ceil_div(g.N, 64);
+// 16-byte loads only (the plan never picks it otherwise: with 4-byte loads
+// 64 x 64 tiles with K groups measured slower than 32 x 32 ones).
+static hipError_t launch_k4_t64_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
+                                    float* ws) {
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true, 2, 4>(g, s, splits, kchunk, ws);
+    return launch_k4_t32_wk4(g, s, splits, kchunk, ws);
+}
+
+// Split-K on top of the tile choice, when the tiles alone leave the chip
+// underused (same sweeps, timed as back-to-back calls so that the second
+// launch, about 2.5 us, counts): with T tiles of the chosen configuration,
+// up to ceil(512 / T) splits, each keeping at least 256 of K, and only when
+// a workgroup's share of K shrinks by at least 512 (64^2 x 65536: 1316 us
+// unsplit on 64 x 64 tiles, 28 us on 32 x 32 with 32 splits; 128^2 x 4096:
+// 85 -> 11.6 us; 256^2 x 16384: 333 -> 32 us; 256^2 x 2048: 44 -> 11 us).
+// Outputs of 64 x 64 tiles or larger are not split: measured within noise
+// or slower once every CU holds a workgroup.  At most 32 splits; chunks are
+// whole slabs.
+SplitPlan k4_plan(const GemmArgs& g, int requested) {
+    const bool vec = vec_ok(g);
+    const int64_t bk = vec ? 32 : 16;
+    const int64_t T128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
+    const int64_t T64 = ceil_div(g.M, 64) * ceil_div(g.N, 64);
+    const int64_t T32 = ceil_div(g.M, 32) * ceil_div(g.N, 32);
+    int cfg;
+    int64_t tiles;
+    if (vec && T128 >= 1024) {
+        cfg = K4_T128;
+        tiles = T128;
+    } else if (T64 >= 512) {
+        cfg = K4_T64;
+        tiles = T64;
+    } else if (T32 <= 256 || !vec) {
+        cfg = K4_T32_WK4;
+        tiles = T32;
+    } else {
+        cfg = K4_T64_WK4;
+        tiles = T64;
+    }
     int64_t S = requested;
     if (S <= 0) {
-        S = std::min<int64_t>(std::min(ceil_div(256, T), g.K / 256), 16);
-        if (S >= 2 && g.K - ceil_div(g.K, S) < 512) S = 1;
+        S = 1;
+        if (cfg == K4_T32_WK4) {
+            S = std::min<int64_t>(std::min(ceil_div(512, tiles), g.K / 256), 32);
+            if (S >= 2 && g.K - ceil_div(g.K, S) < 512) S = 1;
+        }
     }
+    // 128 x 128 tiles have no split variant: a requested split runs on 64 x 64.
+    if (S > 1 && cfg == K4_T128) cfg = K4_T64;
     S = std::min(S, ceil_div(g.K, bk));
-    if (S <= 1) return {1, g.K, 0};
+    if (S <= 1) return {1, g.K, 0, cfg};
     const int64_t kc = ceil_div(ceil_div(g.K, S), bk) * bk;
     S = ceil_div(g.K, kc);
-    return {(int)S, kc, S * g.M * g.N};
+    return {(int)S, kc, S * g.M * g.N, cfg};
 }
 
-static bool uses_tile128(const GemmArgs& g, int requested) {
-    return requested == 0 && vec_ok(g) && ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 1024;
-}
-
-SplitPlan k4_plan(const GemmArgs& g, int requested) {
-    if (uses_tile128(g, requested)) return {1, g.K, 0};
-    return k4_split_plan(g, requested);
+static hipError_t launch_plan(const GemmArgs& g, const SplitPlan& p, float* ws, hipStream_t s) {
+    const int kc = (int)p.kchunk;
+    switch (p.cfg) {
+        case K4_T128: return launch_k4_tile128(g, s);
+        case K4_T64_WK4: return launch_k4_t64_wk4(g, s, p.splits, kc, ws);
+        case K4_T32_WK4: return launch_k4_t32_wk4(g, s, p.splits, kc, ws);
+        default: return launch_k4_t64(g, s, p.splits, kc, ws);
+    }
 }
 
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
-    if (uses_tile128(g, requested)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4>(g, s);
-    const SplitPlan p = k4_split_plan(g, requested);
-    if (p.splits <= 1) return launch_k4_tile64(g, s);
+    SplitPlan p = k4_plan(g, requested);
+    if (p.splits <= 1) return launch_plan(g, p, nullptr, s);
     Workspace ws;
     if (workspace_acquire(size_t(p.ws_floats) * sizeof(float), s, &ws) != hipSuccess) {
         // No workspace: the unsplit kernel gives the same product.
         (void)hipGetLastError();
-        return launch_k4_tile64(g, s);
+        p.splits = 1;
+        return launch_plan(g, p, nullptr, s);
     }
-    const hipError_t e = launch_k4_tile64_split(g, p, static_cast<float*>(ws.ptr), s);
+    const hipError_t e = launch_plan(g, p, static_cast<float*>(ws.ptr), s);
     const hipError_t f = workspace_release(&ws, s);
     return e != hipSuccess ? e : f;
 }

@@ -42,14 +42,15 @@ hipError_t launch_k3_regtile(const GemmArgs& g, hipStream_t s);
 // Tile size and K split chosen by shape; requested_splits > 0 asks for that
 // many K chunks (at most; 1 = never split).
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested_splits = 0);
-// Split-K plan of the matrix-core kernel: `splits` chunks of kchunk (the last
-// one shorter) whose partial products take ws_floats floats of workspace.
+// Plan of the matrix-core kernel for a shape: tile configuration (cfg, an
+// internal id) and K split, `splits` chunks of kchunk (the last one shorter)
+// whose partial products take ws_floats floats of workspace.
 struct SplitPlan {
     int splits;
     int64_t kchunk, ws_floats;
+    int cfg;
 };
-SplitPlan k4_split_plan(const GemmArgs& g, int requested_splits);
-// The plan launch_k4_mfma follows (no split when it picks 128 x 128 tiles).
+// requested_splits 0: split by shape; > 0: at most that many chunks.
 SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
 // Scratch memory for launches that need it: the device's cached buffer,
 // held (with the device's workspace lock) from acquire to release; every

@@ -63,7 +63,7 @@ def run_ex(ta, tb, M, N, K, alpha, beta, dist, seed, pad=0, c0_nan=False):
 
 
 SHAPES = [(1, 1, 1), (7, 5, 3), (33, 65, 17), (129, 257, 33), (300, 17, 129), (256, 256, 256),
-          (65, 129, 257)]
+          (65, 129, 257), (640, 576, 300)]
 COEFS = [(1.0, 0.0), (2.0, 0.5), (-1.5, -2.0), (0.0, 3.0)]
 
 

@@ -102,8 +102,8 @@ def test_split_beta_zero_does_not_read_c():
 
 
 def test_split_one_is_the_unsplit_kernel():
-    # splits = 1 runs the unsplit kernel: bit-identical to sgemm_f32_ex on a
-    # shape the shape-chosen plan would split.
+    # splits = 1 runs the unsplit kernel; splits = 0 and the plain entry
+    # point run the same split plan, bit for bit.
     M, N, K = 128, 128, 4096
     assert rs.split_plan(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)[0] > 1
     A, B = make_operands(M, N, K, "uniform", 3)
@@ -120,8 +120,8 @@ def test_split_one_is_the_unsplit_kernel():
 
 # Shapes the shape-chosen plan splits, at full size through the plain entry
 # point sgemm_f32 (AUTO): every element against the oracle.
-AUTO_SPLIT = [(256, 256, 768, 3), (128, 128, 1024, 4), (128, 128, 4096, 16), (256, 256, 16384, 16),
-              (256, 256, 2048, 8), (200, 120, 3000, 0)]
+AUTO_SPLIT = [(256, 256, 768, 3), (128, 128, 1024, 4), (128, 128, 4096, 16), (256, 256, 16384, 8),
+              (256, 256, 2048, 8), (64, 64, 65536, 32), (512, 512, 4096, 2), (200, 120, 3000, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,want", AUTO_SPLIT, ids=lambda v: str(v))
