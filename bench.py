@@ -306,8 +306,8 @@ SMALL_SHAPES = {
 
 def small_shapes(reps: int, only=None):
     """Per shape: chunks chosen, us per call split (as chosen) and unsplit:
-    back-to-back calls on one stream, so a call's time is the larger of its
-    device time and its host launch cost."""
+    back-to-back calls on one stream (best of three rounds), so a call's time
+    is the larger of its device time and its host launch cost."""
     import torch
     import roofline_sgemm_f32_amd as rs
     from roofline_sgemm_f32_amd import metrics as m
@@ -345,8 +345,12 @@ def small_shapes(reps: int, only=None):
         call(1)()
         torch.cuda.synchronize()
         warm = int(min(5000, max(20, 0.05 / max(time.perf_counter() - t0, 1e-6))))
-        t_auto, _ = time_launches(call(0), reps, warm, per_launch=False)
-        t_one, _ = time_launches(call(1), reps, warm, per_launch=False)
+        # Three alternating rounds, best of each: these calls take a few us,
+        # so host-side jitter would otherwise decide which plan looks faster.
+        t_auto = t_one = float("inf")
+        for _ in range(3):
+            t_auto = min(t_auto, time_launches(call(0), reps, warm, per_launch=False)[0])
+            t_one = min(t_one, time_launches(call(1), reps, warm, per_launch=False)[0])
         rec = {"shape": name, "M": M, "N": N, "K": K, "chunks": chunks, "kchunk": kchunk,
                "us_per_call": round(1e3 * t_auto, 2), "gflops": round(m.gflops(flops, t_auto), 1),
                "unsplit_us_per_call": round(1e3 * t_one, 2),

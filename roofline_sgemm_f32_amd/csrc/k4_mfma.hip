@@ -360,7 +360,7 @@ hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
 // (N and ldc multiples of 4, C 16-byte aligned) moves them as one 16-byte
 // access.  W holds S dense M x N slabs.
 template <bool VEC>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restrict__ C, int64_t ldc,
               float alpha, float beta) {
     const int nq = (N + 3) / 4;
@@ -373,6 +373,7 @@ splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restric
         float* cp = C + (int64_t)r * ldc + c;
         if constexpr (VEC) {
             v4f sum = *(const v4f*)w;
+#pragma unroll 8
             for (int z = 1; z < S; z++) sum += *(const v4f*)(w + z * slab);
             v4f v;
 #pragma unroll
@@ -386,6 +387,7 @@ splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restric
         } else {
             for (int e = 0; e < 4 && c + e < N; e++) {
                 float sum = w[e];
+#pragma unroll 8
                 for (int z = 1; z < S; z++) sum += w[z * slab + e];
                 float v = alpha * sum;
                 if (read_c) v = fmaf(beta, cp[e], v);
@@ -398,12 +400,14 @@ splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restric
 hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, hipStream_t s) {
     const int64_t total = g.M * ceil_div(g.N, 4);
     const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
-    const dim3 grid(grid_for(ceil_div(total, 256)));
+    // One-wave workgroups: the partial slabs are few and small, so spread
+    // them over as many CUs as possible.
+    const dim3 grid(grid_for(ceil_div(total, 64)));
     if (vec)
-        hipLaunchKernelGGL(splitk_reduce<true>, grid, dim3(256), 0, s, (int)g.M, (int)g.N, splits,
+        hipLaunchKernelGGL(splitk_reduce<true>, grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
                            ws, g.C, g.ldc, g.alpha, g.beta);
     else
-        hipLaunchKernelGGL(splitk_reduce<false>, grid, dim3(256), 0, s, (int)g.M, (int)g.N, splits,
+        hipLaunchKernelGGL(splitk_reduce<false>, grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
                            ws, g.C, g.ldc, g.alpha, g.beta);
     return hipGetLastError();
 }

@@ -175,3 +175,23 @@ def test_split_repeated_calls_identical():
     C2 = rs.sgemm_ex(Ad, Bd, splits=8)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
+
+
+# One shape per tile configuration of the plan, split on request: 64 x 64
+# tiles with 4 K groups (16-byte loads, under 512 tiles), 32 x 32 with 4 K
+# groups (4-byte loads), 64 x 64 (512 tiles and more), with both load widths.
+CONFIG_SHAPES = [(640, 576, 300), (641, 577, 301), (2048, 1024, 256), (2049, 1023, 255)]
+
+
+@pytest.mark.parametrize("shape", CONFIG_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1)], ids=["NN", "TT"])
+def test_split_every_config(shape, ta, tb):
+    M, N, K = shape
+    for splits in (2, 5):
+        note(f"[split-cfg] {ta}{tb} {M}x{N}x{K} splits={splits}")
+        got, ref, _, _, chunks = run_split(ta, tb, M, N, K, 1.0, 0.0, splits, dist="int", seed=splits)
+        assert 1 < chunks <= splits  # whole slabs: K = 256 in slabs of 32 takes 4 chunks for 5
+        assert np.array_equal(got.astype(np.float64), ref), (splits, chunks)
+        got, ref, S, E, _ = run_split(ta, tb, M, N, K, 0.75, -1.25, splits, seed=M + splits)
+        rep = check.check_ex(got, ref, S, E, K)
+        assert rep["ok"], rep
