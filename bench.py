@@ -261,7 +261,8 @@ def ladder(args, out):
     import roofline_sgemm_f32_amd as rs
     names = args.ladder_workloads.split(",")
     variants = ["k0_naive", "k1_coalesced", "k2_lds_tiled16", "k2_lds_tiled32", "k2_lds_tiled32_pad1", "k2_lds_tiled16_pad1",
-                "k3_regtile_db", "k4_mfma_tile64", "k4_mfma_tile128", "k4_mfma", "auto"]
+                "k3_regtile_db", "k4_mfma_tile64", "k4_mfma_tile128", "k4_mfma_tile128x256", "k4_mfma",
+                "auto"]
     rows = []
     for name in names:
         w = WORKLOADS[name]

@@ -62,7 +62,8 @@ typedef enum sgemm_variant {
     SGEMM_K2_LDS_TILED16_PAD1 = 8,/* as K2_LDS_TILED16 with rows padded by one float */
     SGEMM_K4_MFMA_TILE128 = 9,    /* K4 with 128 x 128 tiles whatever the shape */
     SGEMM_K4_MFMA_TILE64 = 10,    /* K4 with 64 x 64 tiles whatever the shape */
-    SGEMM_VARIANT_COUNT = 11
+    SGEMM_K4_MFMA_TILE128X256 = 11, /* K4 with 128 x 256 tiles whatever the shape */
+    SGEMM_VARIANT_COUNT = 12
 } sgemm_variant_t;
 
 typedef enum sgemm_status {

@@ -26,6 +26,7 @@ VARIANTS = {
     "k2_lds_tiled16_pad1": 8,
     "k4_mfma_tile128": 9,
     "k4_mfma_tile64": 10,
+    "k4_mfma_tile128x256": 11,
 }
 
 # sgemm_status_t

@@ -118,6 +118,9 @@ int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float*
         case SGEMM_K4_MFMA_TILE64:
             if (!sgemm::k4_supports(g)) return SGEMM_ERR_UNSUPPORTED;
             return launch_status(sgemm::launch_k4_tile64(g, s));
+        case SGEMM_K4_MFMA_TILE128X256:
+            if (!sgemm::k4_supports(g)) return SGEMM_ERR_UNSUPPORTED;
+            return launch_status(sgemm::launch_k4_tile128x256(g, s));
         default: return SGEMM_ERR_VARIANT;
     }
 }
@@ -249,6 +252,7 @@ const char* sgemm_variant_name(int variant) {
         case SGEMM_K0_NAIVE: return "k0_naive";
         case SGEMM_K4_MFMA_TILE128: return "k4_mfma_tile128";
         case SGEMM_K4_MFMA_TILE64: return "k4_mfma_tile64";
+        case SGEMM_K4_MFMA_TILE128X256: return "k4_mfma_tile128x256";
         default: return nullptr;
     }
 }

@@ -87,7 +87,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 // stores the tile.  This shortens each wave's chain of dependent MFMAs by
 // WK without scratch memory or a second launch.
 template <class CF, int OCC, int GM = GROUP_M, bool XCD_REMAP = true, bool SPLIT = false,
-          bool SPLITK = false, int WK = 1>
+          bool SPLITK = false, int WK = 1, bool PRIO = false>
 __global__ void __launch_bounds__(CF::THREADS * WK) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* __restrict__ B,
         int ldb, float* __restrict__ C, int64_t ldc, float alpha, float beta, int tiles_m,
@@ -262,6 +262,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                 // stage are out.
                 asm volatile("" ::: "memory");
                 if (s + NS - 1 < nk) issue(((s + NS - 1) * WK + kg) * CF::BK, (s + NS - 1) % NS);
+                if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
                 mfmas(af, bf);
 #pragma unroll
                 for (int h = 1; h < NH; h++) {
@@ -277,6 +278,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             for (int mb = 0; mb < TM; mb++)
 #pragma unroll
                 for (int nb = 0; nb < TN; nb++) asm volatile("" : "+a"(acc[mb][nb]));
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             // Slab s + 1 landed: the slabs after it may stay in flight.
             const int newer = nk - 2 - s < NS - 2 ? nk - 2 - s : NS - 2;
             wait_vm_batches<PER, NS - 2>(newer > 0 ? newer : 0);
@@ -344,10 +346,10 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     }
 }
 
-template <class CF, int OCC, bool SPLIT = false, int WK = 1>
+template <class CF, int OCC, bool SPLIT = false, int WK = 1, bool PRIO = false>
 hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
-    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, false, WK>), dim3(grid_for(tiles)),
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, false, WK, PRIO>), dim3(grid_for(tiles)),
                        dim3(CF::THREADS * WK), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, g.C, g.ldc,
                        g.alpha, g.beta, (int)tm, (int)tn, (int)tiles, 0);
@@ -496,7 +498,21 @@ static bool vec_ok(const GemmArgs& g) {
 //    (1024 x 1027 x 1024: 41.5 against 52.0).  A wave's chain of dependent
 //    matrix instructions is what bounds these shapes: 32 x 32 tiles give more
 //    workgroups, K groups shorten each chain.
-enum K4Cfg { K4_T128, K4_T64, K4_T64_WK4, K4_T32_WK4 };
+//  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
+//    SIMD, fragments read in halves, raised wave priority during the
+//    matrix instructions) for A and B as stored (no transposes) when the
+//    tiles fill whole rounds of 2 per CU: square 4096 0.956 ms against
+//    0.990 on 128 x 128, square 8192 7.57 against 7.79 ms; with a partial
+//    last round (square 3072, 6144) 128 x 128 is faster, as it is for
+//    B stored transposed.
+enum K4Cfg { K4_T128, K4_T64, K4_T64_WK4, K4_T32_WK4, K4_T128X256 };
+
+hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s) {
+    using k4::Cfg;
+    if (g.trans_a || g.trans_b) return launch_k4_tile128(g, s);
+    if (vec_ok(g)) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true>, 2, true, 1, true>(g, s);
+    return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, false>, 2, true, 1, true>(g, s);
+}
 
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
     if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4, false, 2, 1, false>(g, s);
@@ -512,8 +528,9 @@ hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) { return launch_k4
 
 static hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
                                     float* ws) {
-    if (vec_ok(g)) return launch_k4_orient<1, 1, 1, 1, 32, true, 4, true, 2, 4>(g, s, splits, kchunk, ws);
-    return launch_k4_orient<1, 1, 1, 1, 16, false, 8, false, 2, 4>(g, s, splits, kchunk, ws);
+    // Occupancy targets as the LDS allows them (2 and 4 workgroups per CU).
+    if (vec_ok(g)) return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4>(g, s, splits, kchunk, ws);
+    return launch_k4_orient<1, 1, 1, 1, 16, false, 4, false, 2, 4>(g, s, splits, kchunk, ws);
 }
 
 // 16-byte loads only (the plan never picks it otherwise: with 4-byte loads
@@ -540,9 +557,13 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     const int64_t T128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
     const int64_t T64 = ceil_div(g.M, 64) * ceil_div(g.N, 64);
     const int64_t T32 = ceil_div(g.M, 32) * ceil_div(g.N, 32);
+    const int64_t T256 = ceil_div(g.M, 128) * ceil_div(g.N, 256);
     int cfg;
     int64_t tiles;
-    if (vec && T128 >= 1024) {
+    if (vec && !g.trans_a && !g.trans_b && T256 >= 512 && T256 % 512 == 0) {
+        cfg = K4_T128X256;
+        tiles = T256;
+    } else if (vec && T128 >= 1024) {
         cfg = K4_T128;
         tiles = T128;
     } else if (T64 >= 512) {
@@ -563,8 +584,9 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
             if (S >= 2 && g.K - ceil_div(g.K, S) < 512) S = 1;
         }
     }
-    // 128 x 128 tiles have no split variant: a requested split runs on 64 x 64.
-    if (S > 1 && cfg == K4_T128) cfg = K4_T64;
+    // 128 x 128 and 128 x 256 tiles have no split variant: a requested split
+    // runs on 64 x 64.
+    if (S > 1 && (cfg == K4_T128 || cfg == K4_T128X256)) cfg = K4_T64;
     S = std::min(S, ceil_div(g.K, bk));
     if (S <= 1) return {1, g.K, 0, cfg};
     const int64_t kc = ceil_div(ceil_div(g.K, S), bk) * bk;
@@ -576,6 +598,7 @@ static hipError_t launch_plan(const GemmArgs& g, const SplitPlan& p, float* ws, 
     const int kc = (int)p.kchunk;
     switch (p.cfg) {
         case K4_T128: return launch_k4_tile128(g, s);
+        case K4_T128X256: return launch_k4_tile128x256(g, s);
         case K4_T64_WK4: return launch_k4_t64_wk4(g, s, p.splits, kc, ws);
         case K4_T32_WK4: return launch_k4_t32_wk4(g, s, p.splits, kc, ws);
         default: return launch_k4_t64(g, s, p.splits, kc, ws);

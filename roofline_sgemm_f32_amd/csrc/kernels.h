@@ -65,6 +65,8 @@ hipError_t workspace_acquire(size_t bytes, hipStream_t s, Workspace* ws);
 hipError_t workspace_release(Workspace* ws, hipStream_t s);
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s);
+// 128 x 256 tiles for A and B as stored (transposed operands: 128 x 128).
+hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.
 bool k4_supports(const GemmArgs& g);
 hipError_t launch_zero(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);

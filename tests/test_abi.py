@@ -78,7 +78,7 @@ def test_validation_codes(lib, variant):
 
 
 def test_unknown_variant(lib):
-    assert call(11, 4, 4, 4) == VARIANT
+    assert call(len(rs.VARIANTS), 4, 4, 4) == VARIANT  # one past the last variant
     assert call(-1, 4, 4, 4) == VARIANT
 
 

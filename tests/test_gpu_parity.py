@@ -21,8 +21,8 @@ from tests.gpu_util import run, to_device
 pytestmark = pytest.mark.gpu
 
 ALL = ["k0_naive", "k1_coalesced", "k2_lds_tiled32", "k2_lds_tiled16", "k2_lds_tiled32_pad1", "k2_lds_tiled16_pad1",
-       "k3_regtile_db", "k4_mfma", "k4_mfma_tile128", "k4_mfma_tile64", "auto"]
-FAST = ["k3_regtile_db", "k4_mfma", "k4_mfma_tile128", "k4_mfma_tile64", "auto"]
+       "k3_regtile_db", "k4_mfma", "k4_mfma_tile128", "k4_mfma_tile64", "k4_mfma_tile128x256", "auto"]
+FAST = ["k3_regtile_db", "k4_mfma", "k4_mfma_tile128", "k4_mfma_tile64", "k4_mfma_tile128x256", "auto"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -173,7 +173,7 @@ def test_all_ones_gives_row_sums(variant):
     assert np.all(C == C[:, :1])
 
 
-@pytest.mark.parametrize("variant", ["k4_mfma_tile128", "k4_mfma_tile64"])
+@pytest.mark.parametrize("variant", ["k4_mfma_tile128", "k4_mfma_tile64", "k4_mfma_tile128x256"])
 def test_row_permutation_k4(variant):
     M, N, K = 256, 256, 300
     A, B = make_operands(M, N, K, "normal", seed=41)
@@ -192,7 +192,7 @@ def _sample(n, k, seed):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-@pytest.mark.parametrize("variant", ["auto", "k4_mfma_tile128", "k4_mfma_tile64"])
+@pytest.mark.parametrize("variant", ["auto", "k4_mfma_tile128", "k4_mfma_tile64", "k4_mfma_tile128x256"])
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload(variant, name):
     """The workloads at full size: complete check where the oracle is quick
