@@ -472,12 +472,19 @@ bool k4_supports(const GemmArgs& g) {
            offsets_fit(!g.trans_a, g.lda) && offsets_fit(g.trans_b, g.ldb);
 }
 
+// Whether an operand's rows suit 16-byte loads along its run (the stored
+// row length): aligned rows, and a run in whole 4-float chunks.
+static bool rows_vec(const float* p, int64_t ld, int64_t run) {
+    return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && run % 4 == 0;
+}
+
 static bool vec_ok(const GemmArgs& g) {
-    // 16-byte loads run along each operand's contiguous dimension.
+    // 16-byte loads run along each operand's contiguous dimension; with
+    // padded runs a chunk may straddle the run's end into the zero padding.
     const int64_t a_run = g.trans_a ? g.M : g.K, b_run = g.trans_b ? g.K : g.N;
-    return (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) &&
-           (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
-           a_run % 4 == 0 && b_run % 4 == 0;
+    const int64_t ra = g.runs_padded ? packed_ld(a_run) : a_run;
+    const int64_t rb = g.runs_padded ? packed_ld(b_run) : b_run;
+    return rows_vec(g.A, g.lda, ra) && rows_vec(g.B, g.ldb, rb);
 }
 
 // Tile configurations, chosen from sweeps on MI355X (square 256..8192,
@@ -605,7 +612,61 @@ static hipError_t launch_plan(const GemmArgs& g, const SplitPlan& p, float* ws, 
     }
 }
 
+// Packing pre-pass: operands that do not suit 16-byte loads are copied into
+// zero-padded aligned rows (pack.hip) when the output is large enough for a
+// 64 x 64 or larger tile configuration, where the 16-byte path pays for the
+// copy (3001 x 4099 x 2047: 0.488 ms on 4-byte loads, 0.437 ms + 0.02 ms of
+// packing on 16-byte ones; 4095 x 4097 x 4093: 1.295 -> 1.158 + 0.04 ms).
+// Smaller outputs keep 4-byte loads.
+static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
+    *done = false;
+    if (vec_ok(g)) return hipSuccess;
+    GemmArgs gp = g;
+    gp.runs_padded = true;
+    const int64_t a_rows = g.trans_a ? g.K : g.M, a_run = g.trans_a ? g.M : g.K;
+    const int64_t b_rows = g.trans_b ? g.N : g.K, b_run = g.trans_b ? g.K : g.N;
+    const bool pack_a = !rows_vec(g.A, g.lda, a_run), pack_b = !rows_vec(g.B, g.ldb, b_run);
+    const int64_t a_floats = pack_a ? a_rows * packed_ld(a_run) : 0;
+    const int64_t b_floats = pack_b ? b_rows * packed_ld(b_run) : 0;
+    // Plan as if packed (16-byte loads); the pass is kept for large tiles only.
+    gp.A = pack_a ? reinterpret_cast<const float*>(uintptr_t(256)) : g.A;
+    gp.B = pack_b ? reinterpret_cast<const float*>(uintptr_t(256)) : g.B;
+    if (pack_a) gp.lda = packed_ld(a_run);
+    if (pack_b) gp.ldb = packed_ld(b_run);
+    if (!k4_supports(gp)) return hipSuccess;
+    const SplitPlan p = k4_plan(gp, 0);
+    if (p.splits > 1 || (p.cfg != K4_T64 && p.cfg != K4_T128 && p.cfg != K4_T128X256))
+        return hipSuccess;
+    // B's copy starts on a 256-byte boundary after A's.
+    const size_t a_bytes = (size_t(a_floats) * sizeof(float) + 255) / 256 * 256;
+    Workspace ws;
+    if (workspace_acquire(a_bytes + size_t(b_floats) * sizeof(float), s, &ws) != hipSuccess) {
+        (void)hipGetLastError();
+        return hipSuccess;  // no workspace: the 4-byte path
+    }
+    float* pa = static_cast<float*>(ws.ptr);
+    float* pb = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes);
+    hipError_t e = hipSuccess;
+    if (pack_a) {
+        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, s);
+        gp.A = pa;
+    }
+    if (e == hipSuccess && pack_b) {
+        e = launch_pack(g.B, b_rows, b_run, g.ldb, pb, s);
+        gp.B = pb;
+    }
+    if (e == hipSuccess) e = launch_plan(gp, k4_plan(gp, 0), nullptr, s);
+    const hipError_t f = workspace_release(&ws, s);
+    *done = true;
+    return e != hipSuccess ? e : f;
+}
+
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
+    if (requested == 0) {
+        bool done;
+        const hipError_t e = launch_packed(g, s, &done);
+        if (done || e != hipSuccess) return e;
+    }
     SplitPlan p = k4_plan(g, requested);
     if (p.splits <= 1) return launch_plan(g, p, nullptr, s);
     Workspace ws;

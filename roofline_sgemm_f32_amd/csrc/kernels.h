@@ -21,6 +21,9 @@ struct GemmArgs {
     int64_t ldc;
     bool trans_a = false, trans_b = false;
     float alpha = 1.0f, beta = 0.0f;
+    // Rows of A and B as stored hold their run rounded up to 4 floats, the
+    // extra ones zero (packed operands: see pack.hip).
+    bool runs_padded = false;
 };
 
 // Upper bound on the number of workgroups a launch uses; kernels loop over
@@ -75,6 +78,11 @@ hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta,
 // General (transposes, alpha, beta) one-output-per-lane kernel with 64-bit
 // offsets: the fallback for shapes the matrix-core kernel cannot address.
 hipError_t launch_k1_general(const GemmArgs& g, hipStream_t s);
+// Copy a stored rows x cols matrix (leading dimension ld, any alignment)
+// into dst as rows x packed_ld(cols), zero-padded; dst 16-byte aligned.
+int64_t packed_ld(int64_t cols);
+hipError_t launch_pack(const float* src, int64_t rows, int64_t cols, int64_t ld, float* dst,
+                       hipStream_t s);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, int block, int64_t grid, hipStream_t s);
 int64_t copy_default_grid(int64_t n, int block);
 hipError_t launch_probe_valu(float* out, int64_t iters, float x, float y, int64_t blocks, int block,

@@ -185,3 +185,21 @@ def test_ex_square4096_sampled(ta, tb):
     cols = np.array([0, 63, 64, 3000, 4095])
     ref, S = oracle.sgemm_f64(as_numpy(A), np.ascontiguousarray(as_numpy(B)[:, cols]))
     assert check.check(Cn[:, cols], ref, S, w.K)["ok"]
+
+
+# Outputs large enough for 64 x 64 tiles whose operands do not suit 16-byte
+# loads are packed into zero-padded aligned copies first: both operands, only
+# A (K odd), only B (N odd), in every orientation.
+PACKED = [(1601, 1283, 97), (1600, 1283, 96), (1601, 1284, 97)]
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)], ids=["NN", "NT", "TN", "TT"])
+@pytest.mark.parametrize("shape", PACKED, ids=lambda s: "x".join(map(str, s)))
+def test_ex_packed_operands(ta, tb, shape):
+    M, N, K = shape
+    print(f"[packed] {ta}{tb} {M}x{N}x{K}", flush=True)
+    got, ref, _, _ = run_ex(ta, tb, M, N, K, 2.0, -1.0, "int", seed=M + K)
+    assert np.array_equal(got.astype(np.float64), ref)
+    got, ref, S, E = run_ex(ta, tb, M, N, K, 1.5, 0.5, "uniform", seed=N + K, pad=1)
+    rep = check.check_ex(got, ref, S, E, K)
+    assert rep["ok"], rep
