@@ -373,7 +373,7 @@ def main():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="square4096", choices=sorted(WORKLOADS))
     p.add_argument("--variant", default="auto")
     p.add_argument("--cpu-seconds", type=float, default=12.0,

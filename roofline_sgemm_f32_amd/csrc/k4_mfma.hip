@@ -491,11 +491,14 @@ static bool vec_ok(const GemmArgs& g) {
 // K-heavy 64^2 x 65536 .. 1024^2 x 4096, skinny and unaligned shapes; every
 // sweep row checked bit-exact against a reference on integer data):
 //  * T128: 128 x 128 tiles, 4 waves of 2 x 2 accumulators, K slabs of 16,
-//    4 waves per SIMD: best once there are at least 1024 tiles (4 per CU),
-//    e.g. square 4096 and 8192;
+//    4 waves per SIMD: with at least two rounds of 1024 tiles (4 per CU) or
+//    whole rounds (square 6144: 3.34 ms against 3.62 on 64 x 64; 7168: 5.56
+//    against 5.72), and for transposed operands at square 4096;
 //  * T64: 64 x 64 tiles, 4 waves of 1 accumulator, K slabs of 32 with
 //    16-byte loads (fragments read in two halves: 7 % on square 1024), of 16
-//    with 4-byte loads: from 512 tiles up (2048^2, 3001 x 4099 x 2047);
+//    with 4-byte loads: from 512 tiles up, when the larger tiles would leave
+//    a partial round (square 3072 0.488 ms against 0.575 on 128 x 128; 4608
+//    1.60 against 1.68; 5120 2.11 against 2.17; 3001 x 4099 x 2047);
 //  * T64_WK4: the same tile with 4 K groups (16 waves): below 512 such tiles
 //    with 16-byte loads (square 1024: 24.1 us against 25.1; 1024^2 x 4096:
 //    79.8 against 86.9);
@@ -508,10 +511,11 @@ static bool vec_ok(const GemmArgs& g) {
 //  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
 //    SIMD, fragments read in halves, raised wave priority during the
 //    matrix instructions) for A and B as stored (no transposes) when the
-//    tiles fill whole rounds of 2 per CU: square 4096 0.956 ms against
-//    0.990 on 128 x 128, square 8192 7.57 against 7.79 ms; with a partial
-//    last round (square 3072, 6144) 128 x 128 is faster, as it is for
-//    B stored transposed.
+//    tiles fill whole rounds of 2 per CU, or the last round at least 3/4:
+//    square 4096 0.956 ms against 0.990 on 128 x 128, 8192 7.57 against
+//    7.79 ms, 5632 2.63 against 2.71; with a smaller last round (square
+//    3072, 4608, 6144) it is the slowest of the three, and with B stored
+//    transposed 128 x 128 is as fast.
 enum K4Cfg { K4_T128, K4_T64, K4_T64_WK4, K4_T32_WK4, K4_T128X256 };
 
 hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s) {
@@ -567,10 +571,13 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     const int64_t T256 = ceil_div(g.M, 128) * ceil_div(g.N, 256);
     int cfg;
     int64_t tiles;
-    if (vec && !g.trans_a && !g.trans_b && T256 >= 512 && T256 % 512 == 0) {
+    // Large tiles pay off only when the workgroups fill their rounds: a
+    // partial last round of 128 x 256 (2 per CU) costs about a full one, of
+    // 128 x 128 (4 per CU) about its share.
+    if (vec && !g.trans_a && !g.trans_b && T256 >= 512 && (T256 % 512 == 0 || T256 % 512 >= 384)) {
         cfg = K4_T128X256;
         tiles = T256;
-    } else if (vec && T128 >= 1024) {
+    } else if (vec && (T128 >= 2048 || (T128 >= 1024 && T128 % 1024 == 0))) {
         cfg = K4_T128;
         tiles = T128;
     } else if (T64 >= 512) {
