@@ -10,10 +10,14 @@ over bandwidth.
 
 Input is a counter summary written from rocprofv3 runs (the table in
 ``profiles/ladder_<workload>_counters.txt``: per-kernel duration, counted
-FLOP, HBM bytes read and written).  Output: a markdown table and an SVG plot.
+FLOP, HBM bytes read and written), or with ``--small`` a bench.py JSON line
+whose small-shape section is placed at algorithmic intensity and measured
+time per call.  Output: a markdown table and an SVG plot.
 
     python -m roofline_sgemm_f32_amd.report profiles/ladder_square4096_counters.txt \\
         --md profiles/roofline_square4096.md --svg profiles/roofline_square4096.svg
+    python -m roofline_sgemm_f32_amd.report bench.out --small \\
+        --md profiles/roofline_small_shapes.md --svg profiles/roofline_small_shapes.svg
 """
 from __future__ import annotations
 
@@ -76,16 +80,21 @@ def classify(p: Point, peak_tflops: float, bw_gbs: float) -> dict:
             "roof_tflops": roof, "pct_of_roof": 100.0 * p.tflops / roof if roof else 0.0}
 
 
-def markdown(rows: list[dict], peak_tflops: float, bw_gbs: float, title: str) -> str:
+COUNTED = "Intensity and bandwidth use counted HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated)."
+ALGORITHMIC = ("Intensity and bandwidth use algorithmic bytes (A and B read once, C written once); "
+               "times are per call, back-to-back, host launch cost included.")
+
+
+def markdown(rows: list[dict], peak_tflops: float, bw_gbs: float, title: str, note: str = COUNTED) -> str:
     ridge = m.ridge_flop_per_byte(peak_tflops * 1e3, bw_gbs)
     out = [f"# {title}", "",
            f"Roofs: FP32 {peak_tflops:.1f} TFLOP/s, HBM {bw_gbs / 1e3:.1f} TB/s; ridge {ridge:.1f} FLOP/B.",
-           "Intensity and bandwidth use counted HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated).", "",
+           note, "",
            "| kernel | ms | FLOP/B | TFLOP/s | GB/s | HBM % | FP32 % | bound | % of its roof |",
            "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         ai = "inf" if math.isinf(r["intensity"]) else f"{r['intensity']:.1f}"
-        out.append(f"| {r['kernel']} | {r['ms']:.3f} | {ai} | {r['tflops']:.2f} | {r['gbs']:.0f} | "
+        out.append(f"| {r['kernel']} | {r['ms']:.4f} | {ai} | {r['tflops']:.2f} | {r['gbs']:.0f} | "
                    f"{r['mem_pct']:.1f} | {r['compute_pct']:.1f} | {r['bound']} | {r['pct_of_roof']:.1f} |")
     return "\n".join(out) + "\n"
 
@@ -135,17 +144,48 @@ def svg(rows: list[dict], peak_tflops: float, bw_gbs: float, title: str) -> str:
     return "\n".join(s) + "\n"
 
 
+def small_shape_points(bench_line: dict) -> list[Point]:
+    """Points of the small-shape section of a bench.py JSON line: per shape,
+    the plan the library chose and the unsplit one, at their measured time
+    per call (back-to-back calls, so host launch cost included) and the
+    algorithmic traffic (A and B read once, C written once)."""
+    pts = []
+    for r in bench_line.get("small_shapes") or []:
+        M, N, K = r["M"], r["N"], r["K"]
+        flop = m.sgemm_flops(M, N, K)
+        rd = 4.0 * (M * K + K * N) / 1e6
+        wr = 4.0 * M * N / 1e6
+        pts.append(Point(f"{r['shape']} ({r['chunks']} chunk{'s' if r['chunks'] > 1 else ''})",
+                         r["us_per_call"] / 1e3, flop, rd, wr))
+        if r["chunks"] > 1:
+            pts.append(Point(f"{r['shape']} unsplit", r["unsplit_us_per_call"] / 1e3, flop, rd, wr))
+    return pts
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="roofline report from a counter summary")
-    ap.add_argument("table")
+    ap.add_argument("table", help="counter summary, or a bench.py JSON line file with --small")
+    ap.add_argument("--small", action="store_true",
+                    help="the table is bench.py output: report its small-shape section")
     ap.add_argument("--md")
     ap.add_argument("--svg")
     ap.add_argument("--peak-tflops", type=float, default=m.MI355X_FP32_PEAK_GFLOPS / 1e3)
     ap.add_argument("--bw-gbs", type=float, default=m.MI355X_HBM_GBS)
     ap.add_argument("--title", default="MI355X FP32 roofline, square4096 ladder")
     a = ap.parse_args(argv)
-    rows = [classify(p, a.peak_tflops, a.bw_gbs) for p in parse_counter_table(a.table)]
-    md = markdown(rows, a.peak_tflops, a.bw_gbs, a.title)
+    if a.small:
+        import json
+        line = None
+        for ln in open(a.table):
+            if ln.lstrip().startswith("{") and '"small_shapes"' in ln:
+                line = json.loads(ln)
+        if line is None:
+            raise SystemExit(f"{a.table}: no bench.py line with a small-shape section")
+        pts = small_shape_points(line)
+    else:
+        pts = parse_counter_table(a.table)
+    rows = [classify(p, a.peak_tflops, a.bw_gbs) for p in pts]
+    md = markdown(rows, a.peak_tflops, a.bw_gbs, a.title, ALGORITHMIC if a.small else COUNTED)
     if a.md:
         open(a.md, "w").write(md)
     else:

@@ -47,3 +47,17 @@ def test_parse_and_render(tmp_path):
     assert "| k4 |" in md and "compute" in md and "memory" in md
     s = report.svg(rows, PEAK, BW, "t")
     assert s.startswith("<svg") and s.count("<circle") == 4
+
+
+def test_small_shape_points():
+    line = {"small_shapes": [
+        {"shape": "square256", "M": 256, "N": 256, "K": 256, "chunks": 1, "us_per_call": 5.0,
+         "unsplit_us_per_call": 5.0},
+        {"shape": "kheavy", "M": 128, "N": 128, "K": 4096, "chunks": 16, "us_per_call": 13.0,
+         "unsplit_us_per_call": 30.0}]}
+    pts = report.small_shape_points(line)
+    assert [p.kernel for p in pts] == ["square256 (1 chunk)", "kheavy (16 chunks)", "kheavy unsplit"]
+    # 2 * 256^3 FLOP in 5 us; algorithmic bytes 4 * 3 * 256^2.
+    assert pts[0].tflops == pytest.approx(2 * 256 ** 3 / 5e-6 / 1e12)
+    assert pts[0].intensity == pytest.approx(2 * 256 ** 3 / (12 * 256 ** 2))
+    assert pts[2].ms == pytest.approx(0.030)
