@@ -41,11 +41,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(files=("k4_mfma.hip",)) -> str:
+def kernel_source_hash(files=("k4_mfma.hip", "k4_layout.h")) -> str:
+    """Hash of the matrix-core kernel's code (comments and blank lines
+    dropped, so that editing a comment keeps recorded counters valid)."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "roofline_sgemm_f32_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "roofline_sgemm_f32_amd", "csrc", f)) as fh:
+            for ln in fh:
+                code = re.sub(r"//.*", "", ln).strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -10,20 +10,25 @@
 //
 // Structure (geometry and LDS layouts in k4_layout.h):
 //  * a workgroup owns a BM x BN tile of C; each wave TM x TN accumulators;
-//  * K is consumed in slabs of BK, double-buffered in LDS with one barrier
-//    per slab: read this slab's fragments, issue the next slab's loads into
-//    the other stage, run the slab's MFMAs, wait for the loads, barrier;
+//  * K is consumed in slabs of BK through NSTAGE LDS stages (2 in every
+//    configuration used) with one barrier per slab: read this slab's
+//    fragments, issue the loads of the slab NSTAGE - 1 ahead, run the slab's
+//    MFMAs, wait for the next slab's loads, barrier;
 //  * global -> LDS uses buffer loads that write LDS directly
 //    (buffer_load_dword[x4] ... lds), so staged data never occupies VGPRs;
 //  * elements outside the matrix get a buffer offset past the descriptor's
 //    range, which the hardware returns as zero: edge tiles and the K tail run
 //    the same code; stores are masked only in edge tiles;
-//  * 16-byte loads when both operands are 16-byte aligned and lda, ldb, K, N
-//    are multiples of 4, else 4-byte loads (same LDS image either way);
+//  * 16-byte loads when each operand's stored rows are 16-byte aligned and
+//    hold whole 4-float chunks (or are zero-padded copies from pack.hip),
+//    else 4-byte loads (same LDS image either way);
 //  * tile order: workgroup ids are dealt to the 8 XCDs round-robin, so ids
 //    are remapped to give each XCD a contiguous range of tiles, walked in
 //    groups of GROUP_M tile-rows so that resident tiles share A and B panels
-//    in that XCD's L2.
+//    in that XCD's L2;
+//  * options for small outputs: K groups inside the workgroup (WK) and a
+//    split-K mode across workgroups (SPLITK, with a second reduction kernel);
+//    for the largest tiles, raised wave priority during the MFMAs (PRIO).
 #include <algorithm>
 
 #include "k4_layout.h"
