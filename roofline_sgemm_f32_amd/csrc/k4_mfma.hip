@@ -501,12 +501,16 @@ static bool vec_ok(const GemmArgs& g) {
 //    against 5.72), and for transposed operands at square 4096;
 //  * T64: 64 x 64 tiles, 4 waves of 1 accumulator, K slabs of 32 with
 //    16-byte loads (fragments read in two halves: 7 % on square 1024), of 16
-//    with 4-byte loads: from 512 tiles up, when the larger tiles would leave
+//    with 4-byte loads: from 512 tiles up (more than 256 with 16-byte loads
+//    and more than 256 tiles of 32 x 32), when the larger tiles would leave
 //    a partial round (square 3072 0.488 ms against 0.575 on 128 x 128; 4608
 //    1.60 against 1.68; 5120 2.11 against 2.17; 3001 x 4099 x 2047);
-//  * T64_WK4: the same tile with 4 K groups (16 waves): below 512 such tiles
-//    with 16-byte loads (square 1024: 24.1 us against 25.1; 1024^2 x 4096:
-//    79.8 against 86.9);
+//  * T64_WK4: the same tile with 4 K groups (16 waves, one workgroup per CU
+//    by LDS): up to 256 such tiles with 16-byte loads (square 1024: 23.9 us
+//    against 24.2; 1024^2 x 4096: 79.8 against 86.9).  Between 256 and 512
+//    tiles a second round of these workgroups costs more than the groups
+//    save, and plain 64 x 64 tiles win (1536 x 1024 x 1024: 40.2 us against
+//    45.3; 1280^3: 49.3 against 54.7; 1408^2 x 2048: 76.5 against 83.0);
 //  * T32_WK4: 32 x 32 tiles, one wave per K group, 4 groups: outputs of at
 //    most 256 such tiles (square 256: 5.0 us against 7.9; square 512: 6.9
 //    against 13.2), and with 4-byte loads below 512 tiles of 64 x 64 as well
@@ -585,7 +589,7 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     } else if (vec && (T128 >= 2048 || (T128 >= 1024 && T128 % 1024 == 0))) {
         cfg = K4_T128;
         tiles = T128;
-    } else if (T64 >= 512) {
+    } else if (T64 >= 512 || (vec && T64 > 256 && T32 > 256)) {
         cfg = K4_T64;
         tiles = T64;
     } else if (T32 <= 256 || !vec) {
@@ -646,6 +650,7 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     if (pack_a) gp.lda = packed_ld(a_run);
     if (pack_b) gp.ldb = packed_ld(b_run);
     if (!k4_supports(gp)) return hipSuccess;
+    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512) return hipSuccess;
     const SplitPlan p = k4_plan(gp, 0);
     if (p.splits > 1 || (p.cfg != K4_T64 && p.cfg != K4_T128 && p.cfg != K4_T128X256))
         return hipSuccess;
