@@ -663,15 +663,16 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     }
     float* pa = static_cast<float*>(ws.ptr);
     float* pb = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes);
-    hipError_t e = hipSuccess;
-    if (pack_a) {
-        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, s);
-        gp.A = pa;
-    }
-    if (e == hipSuccess && pack_b) {
-        e = launch_pack(g.B, b_rows, b_run, g.ldb, pb, s);
-        gp.B = pb;
-    }
+    // One launch packs both operands when both need it.
+    hipError_t e;
+    if (pack_a && pack_b)
+        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, g.B, b_rows, b_run, g.ldb, pb, s);
+    else if (pack_a)
+        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, nullptr, 0, 0, 0, nullptr, s);
+    else
+        e = launch_pack(g.B, b_rows, b_run, g.ldb, pb, nullptr, 0, 0, 0, nullptr, s);
+    if (pack_a) gp.A = pa;
+    if (pack_b) gp.B = pb;
     if (e == hipSuccess) e = launch_plan(gp, k4_plan(gp, 0), nullptr, s);
     const hipError_t f = workspace_release(&ws, s);
     *done = true;

@@ -79,9 +79,11 @@ hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta,
 // offsets: the fallback for shapes the matrix-core kernel cannot address.
 hipError_t launch_k1_general(const GemmArgs& g, hipStream_t s);
 // Copy a stored rows x cols matrix (leading dimension ld, any alignment)
-// into dst as rows x packed_ld(cols), zero-padded; dst 16-byte aligned.
+// into dst as rows x packed_ld(cols), zero-padded; dst 16-byte aligned.  A
+// second matrix (src2 not null) is packed by the same launch.
 int64_t packed_ld(int64_t cols);
 hipError_t launch_pack(const float* src, int64_t rows, int64_t cols, int64_t ld, float* dst,
+                       const float* src2, int64_t rows2, int64_t cols2, int64_t ld2, float* dst2,
                        hipStream_t s);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, int block, int64_t grid, hipStream_t s);
 int64_t copy_default_grid(int64_t n, int block);
