@@ -150,7 +150,7 @@ def device_operands(w):
     return A_h, B_h, A, B, C
 
 
-def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float):
+def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float, threads: int | None = None):
     """Time the CPU oracle on a bounded sample of rows of the same product,
     and check the GPU's rows against it."""
     import numpy as np
@@ -159,7 +159,7 @@ def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float):
     from roofline_sgemm_f32_amd import metrics as m
     from roofline_sgemm_f32_amd.inputs import as_numpy
     An, Bn = as_numpy(A_h), as_numpy(B_h)
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     oracle.load()
     rng = np.random.default_rng(0)
     # Calibrate on one row per thread, then size the sample to the budget:
@@ -374,6 +374,43 @@ def small_shapes(reps: int, only=None):
     return rows
 
 
+def cpu_all(seconds: float):
+    """Every workload: the AUTO product on the GPU (mean of back-to-back
+    launches) beside the CPU oracle on a bounded sample of the same product
+    (all host threads; one thread too for the two small squares), with the
+    oracle's rows gating the GPU's.  One JSON line per workload."""
+    import torch
+    from roofline_sgemm_f32_amd import metrics as m
+    from roofline_sgemm_f32_amd.inputs import WORKLOADS
+    rows = []
+    for name, w in WORKLOADS.items():
+        A_h, B_h, A, B, C = device_operands(w)
+        fn = run_gemm_factory("auto", A, B, C)
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        # Back-to-back calls for about 0.5 s (at least 5), after as many warm-ups.
+        steps = int(max(5, min(2000, 0.5 / max(time.perf_counter() - t0, 1e-6))))
+        ms, _ = time_launches(fn, steps, steps, per_launch=False)
+        gpu = m.gflops(m.sgemm_flops(w.M, w.N, w.K), ms)
+        cpu, gate = cpu_baseline_leg(w, A_h, B_h, C, seconds)
+        rec = {"workload": name, "gpu_gflops": round(gpu, 1), "gpu_ms": round(ms, 5),
+               "cpu": cpu, "gpu_over_cpu": round(gpu / cpu["value"], 1), "gate": gate}
+        if w.M <= 1024:
+            one, _ = cpu_baseline_leg(w, A_h, B_h, C, seconds / 2, threads=1)
+            rec["cpu_single_thread"] = one
+        rows.append(rec)
+        log(f"  {name:22s} GPU {gpu:10.1f} GFLOP/s  CPU {cpu['value']:8.2f} GFLOP/s ({cpu['cores']} threads)"
+            f"  x{rec['gpu_over_cpu']}  gate {'ok' if gate['ok'] else 'FAILED'}"
+            + (f"  1 thread {rec['cpu_single_thread']['value']:.2f}" if "cpu_single_thread" in rec else ""))
+        print(json.dumps({"cpu_all": rec}), flush=True)
+        del A, B, C
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     from roofline_sgemm_f32_amd.inputs import WORKLOADS
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -396,6 +433,8 @@ def main():
                    help="calls timed per small shape (0 skips the small-shape section)")
     p.add_argument("--small-only", default=None,
                    help="comma-separated small shapes: time only these and print their JSON")
+    p.add_argument("--cpu-all", action="store_true",
+                   help="only: every workload on the GPU beside the CPU oracle (one JSON line each)")
     args = p.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -413,6 +452,9 @@ def main():
         sys.exit(1)
     rs.load()  # raises when the HIP library is missing: no fallback
     out = open(args.out, "a") if args.out else None
+    if args.cpu_all:
+        ok = all(r["gate"]["ok"] for r in cpu_all(args.cpu_seconds))
+        sys.exit(0 if ok else 3)
     if args.small_only:
         print(json.dumps({"small_shapes": small_shapes(max(args.small_reps, 1),
                                                        args.small_only.split(","))}), flush=True)
