@@ -126,7 +126,10 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
  * gets a buffer of its own, freed stream-ordered after the call.  Split calls
  * on one device take the buffer in turn (a host lock around their launches;
  * a call on another stream than the previous one waits for it on the GPU).
- * If the workspace cannot be allocated the product runs unsplit.
+ * If the workspace cannot be allocated the product runs unsplit, and so do
+ * calls made while `stream` is being captured into a graph (the workspace
+ * paths, split-K and the packing of unaligned operands, are skipped there,
+ * so that every entry point can be captured).
  *   splits == 0: chosen by shape (what sgemm_f32 and sgemm_f32_ex do);
  *   splits == 1: never split;
  *   2 <= splits <= SGEMM_MAX_SPLITS: at most that many chunks (fewer when K

@@ -679,13 +679,29 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     return e != hipSuccess ? e : f;
 }
 
+// Whether work on s is being captured into a graph.  The workspace paths
+// (split-K, packing) allocate stream-ordered memory and order uses across
+// streams with an event, which a capture cannot take part in; captured
+// calls run the unsplit kernel on the operands as stored instead, so every
+// entry point can be captured.
+static bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
+
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
-    if (requested == 0) {
+    const bool in_graph = capturing(s);
+    if (requested == 0 && !in_graph) {
         bool done;
         const hipError_t e = launch_packed(g, s, &done);
         if (done || e != hipSuccess) return e;
     }
     SplitPlan p = k4_plan(g, requested);
+    if (in_graph) p.splits = 1;
     if (p.splits <= 1) return launch_plan(g, p, nullptr, s);
     Workspace ws;
     if (workspace_acquire(size_t(p.ws_floats) * sizeof(float), s, &ws) != hipSuccess) {
