@@ -470,7 +470,10 @@ def main():
     fn = run_gemm_factory(variant, A, B, C)
     log(f"[bench] {w.name} {w.M}x{w.N}x{w.K} variant={variant} ({resolved}) "
         f"warmup={args.warmup} steps={args.steps}")
-    ms_step, ms_launch = time_launches(fn, args.steps, args.warmup)
+    # The timed region is the K back-to-back launches between two events on
+    # the launch stream; the average launch duration is the step time.
+    ms_step, _ = time_launches(fn, args.steps, args.warmup, per_launch=False)
+    ms_launch = ms_step
     flops = m.sgemm_flops(w.M, w.N, w.K)
     value = m.gflops(flops, ms_step)
     achieved_tf = flops / (ms_launch / 1e3) / 1e12
