@@ -259,6 +259,30 @@ def compute_probe(valu_iters=4096, mfma_iters=4096, steps=30, warmup=10):
             "launches": steps}
 
 
+def row_gate(A_h, B_h):
+    """Correctness gate for a timed GPU product outside the headline leg (a
+    ladder row, a small-shape plan): a few rows of C (first, last and some
+    between) against numpy's float64 product of the same host operands, with
+    the binary32 dot-product bound 4 K 2^-24 sum|a b| per element.  Its
+    throughput is printed only when the result passes."""
+    import numpy as np
+    from roofline_sgemm_f32_amd.inputs import as_numpy
+    M, K = A_h.shape
+    rows = sorted({0, 1 % M, M // 3, M // 2, max(M - 2, 0), M - 1})
+    A64 = as_numpy(A_h)[rows].astype(np.float64)
+    B64 = as_numpy(B_h).astype(np.float64)
+    ref = A64 @ B64
+    tol = 4.0 * K * 2.0 ** -24 * (np.abs(A64) @ np.abs(B64))
+
+    def check(C):
+        got = C[rows].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        ok = bool(np.all(err <= tol))  # False on any NaN
+        util = float(np.max(err / np.where(tol > 0, tol, 1.0))) if ok else None
+        return ok, (round(util, 4) if util is not None else None)
+    return check
+
+
 def ladder(args, out):
     """Every variant on every selected workload: the results table."""
     import torch
@@ -274,6 +298,7 @@ def ladder(args, out):
         w = WORKLOADS[name]
         A_h, B_h, A, B, C = device_operands(w)
         flops = m.sgemm_flops(w.M, w.N, w.K)
+        gate = row_gate(A_h, B_h)
         base_ms = None
         for v in variants:
             fn = run_gemm_factory(v, A, B, C)
@@ -285,10 +310,16 @@ def ladder(args, out):
             one = time.perf_counter() - t0
             reps = int(max(1, min(args.ladder_reps, 3.0 / max(one, 1e-6))))
             total, per = time_launches(fn, reps, 1)
+            ok, util = gate(C)
+            if not ok:
+                log(f"  {name:22s} {v:22s} outside the error bound on the gate rows: no throughput")
+                rows.append({"workload": name, "variant": v, "gate": False, "bound_util": util})
+                continue
             g = m.gflops(flops, per)
             if v == "k0_naive":
                 base_ms = per
-            rec = {"workload": name, "variant": v, "ms": round(per, 4), "gflops": round(g, 1),
+            rec = {"workload": name, "variant": v, "gate": True, "bound_util": util,
+                   "ms": round(per, 4), "gflops": round(g, 1),
                    "pct_peak": round(m.pct_of_peak(g, m.MI355X_FP32_PEAK_GFLOPS), 2),
                    "speedup_vs_naive": round(base_ms / per, 2) if base_ms else None, "reps": reps}
             rows.append(rec)
@@ -330,7 +361,7 @@ def small_shapes(reps: int, only=None):
             continue
         if dims is None:
             w = WORKLOADS[name]
-            _, _, A, B, C = device_operands(w)
+            A_h, B_h, A, B, C = device_operands(w)
         else:
             M, N, K = dims
             A_h, B_h = make_operands(M, N, K, "uniform", seed=100 + len(rows))
@@ -358,10 +389,19 @@ def small_shapes(reps: int, only=None):
         # Three alternating rounds, best of each: these calls take a few us,
         # so host-side jitter would otherwise decide which plan looks faster.
         t_auto = t_one = float("inf")
+        gate = row_gate(A_h, B_h)
+        ok = True
         for _ in range(3):
             t_auto = min(t_auto, time_launches(call(0), reps, warm, per_launch=False)[0])
+            ok = ok and gate(C)[0]
             t_one = min(t_one, time_launches(call(1), reps, warm, per_launch=False)[0])
-        rec = {"shape": name, "M": M, "N": N, "K": K, "chunks": chunks, "kchunk": kchunk,
+            ok = ok and gate(C)[0]
+        if not ok:
+            log(f"  small {name:22s} outside the error bound on the gate rows: no throughput")
+            rows.append({"shape": name, "M": M, "N": N, "K": K, "gate": False})
+            del A, B, C
+            continue
+        rec = {"shape": name, "gate": True, "M": M, "N": N, "K": K, "chunks": chunks, "kchunk": kchunk,
                "us_per_call": round(1e3 * t_auto, 2), "gflops": round(m.gflops(flops, t_auto), 1),
                "unsplit_us_per_call": round(1e3 * t_one, 2),
                "unsplit_gflops": round(m.gflops(flops, t_one), 1),

@@ -151,6 +151,8 @@ def small_shape_points(bench_line: dict) -> list[Point]:
     algorithmic traffic (A and B read once, C written once)."""
     pts = []
     for r in bench_line.get("small_shapes") or []:
+        if r.get("gate") is False:
+            continue  # no throughput was measured for a failed result
         M, N, K = r["M"], r["N"], r["K"]
         flop = m.sgemm_flops(M, N, K)
         rd = 4.0 * (M * K + K * N) / 1e6

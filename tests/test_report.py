@@ -54,7 +54,8 @@ def test_small_shape_points():
         {"shape": "square256", "M": 256, "N": 256, "K": 256, "chunks": 1, "us_per_call": 5.0,
          "unsplit_us_per_call": 5.0},
         {"shape": "kheavy", "M": 128, "N": 128, "K": 4096, "chunks": 16, "us_per_call": 13.0,
-         "unsplit_us_per_call": 30.0}]}
+         "unsplit_us_per_call": 30.0},
+        {"shape": "failed", "M": 64, "N": 64, "K": 64, "gate": False}]}
     pts = report.small_shape_points(line)
     assert [p.kernel for p in pts] == ["square256 (1 chunk)", "kheavy (16 chunks)", "kheavy unsplit"]
     # 2 * 256^3 FLOP in 5 us; algorithmic bytes 4 * 3 * 256^2.
