@@ -342,6 +342,7 @@ SMALL_SHAPES = {
     "kheavy128x128x4096": (128, 128, 4096),
     "kheavy256x256x16384": (256, 256, 16384),
     "kheavy1024x1024x4096": (1024, 1024, 4096),
+    "skinny64x8192x8192": (64, 8192, 8192),
 }
 
 

@@ -563,14 +563,58 @@ static hipError_t launch_k4_t64_wk4(const GemmArgs& g, hipStream_t s, int splits
 
 // Split-K on top of the tile choice, when the tiles alone leave the chip
 // underused (same sweeps, timed as back-to-back calls so that the second
-// launch, about 2.5 us, counts): with T tiles of the chosen configuration,
-// up to ceil(512 / T) splits, each keeping at least 256 of K, and only when
-// a workgroup's share of K shrinks by at least 512 (64^2 x 65536: 1316 us
-// unsplit on 64 x 64 tiles, 28 us on 32 x 32 with 32 splits; 128^2 x 4096:
-// 85 -> 11.6 us; 256^2 x 16384: 333 -> 32 us; 256^2 x 2048: 44 -> 11 us).
-// Outputs of 64 x 64 tiles or larger are not split: measured within noise
-// or slower once every CU holds a workgroup.  At most 32 splits; chunks are
-// whole slabs.
+// launch, about 2.5 us, counts).
+//  * 32 x 32 tiles with K groups: with T tiles, up to ceil(512 / T) splits,
+//    each keeping at least 256 of K, and only when a workgroup's share of K
+//    shrinks by at least 512 (64^2 x 65536: 1316 us unsplit on 64 x 64
+//    tiles, 28 us on 32 x 32 with 32 splits; 128^2 x 4096: 85 -> 11.6 us;
+//    256^2 x 16384: 333 -> 32 us; 256^2 x 2048: 44 -> 11 us).
+//  * 64 x 64 tiles (16-byte loads, fewer than 1024 tiles, i.e. under 4 per
+//    CU): the split count from a cost model, below, when it saves at least
+//    5 % over the unsplit choice.  At most 16 splits of at least 512 of K.
+// Chunks are whole slabs.
+namespace {
+constexpr int kCUs = 256;
+// Sustained rate of one CU running n = 1..4 of the 64 x 64 workgroups, and
+// of one CU running the 4-K-group 64 x 64 workgroup, in FLOP per us; fixed
+// cost of a launch, and the split reduction's launch and bandwidth (bytes
+// per us).  Fitted to sweeps of 64..2048 x 64..16384 x 1024..16384 outputs
+// on MI355X (mean error 2 %).
+constexpr double kRate64[5] = {0.0, 0.405e6, 0.462e6, 0.475e6, 0.487e6};
+constexpr double kRate64Wk4 = 0.43e6;
+constexpr double kLaunchUs = 4.0, kReduceUs = 2.5, kReduceBytesPerUs = 5e6;
+
+// Estimated time of T 64 x 64 tiles over S chunks of kc of K: each CU runs
+// c = ceil(T S / 256) workgroups one after another at the rate c of them
+// sustain together, plus the reduction (S partial products read, C written).
+double t64_time_us(const GemmArgs& g, int64_t T, int64_t kc, int64_t S) {
+    const int64_t c = ceil_div(T * S, kCUs);
+    double t = kLaunchUs + double(c) * double(kc) * 8192.0 / kRate64[c < 4 ? c : 4];
+    if (S > 1) t += kReduceUs + 4.0 * double(g.M) * double(g.N) * double(S + 1) / kReduceBytesPerUs;
+    return t;
+}
+
+// Chunk count for 64 x 64 tiles by the model (1: no split pays).  wk4: the
+// unsplit choice is the 4-K-group workgroup (one per CU) rather than plain
+// 64 x 64 tiles.
+int64_t t64_model_splits(const GemmArgs& g, int64_t T, bool wk4) {
+    const double base = wk4 ? kLaunchUs + double(g.K) * 8192.0 / kRate64Wk4 : t64_time_us(g, T, g.K, 1);
+    double best = 0.95 * base;
+    int64_t pick = 1;
+    for (int64_t s = 2; s <= 16; s++) {
+        const int64_t kc = ceil_div(ceil_div(g.K, s), 32) * 32;
+        if (kc < 512) break;
+        const int64_t se = ceil_div(g.K, kc);
+        const double t = t64_time_us(g, T, kc, se);
+        if (t < best) {
+            best = t;
+            pick = se;
+        }
+    }
+    return pick;
+}
+}  // namespace
+
 SplitPlan k4_plan(const GemmArgs& g, int requested) {
     const bool vec = vec_ok(g);
     const int64_t bk = vec ? 32 : 16;
@@ -599,9 +643,15 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
         cfg = K4_T64_WK4;
         tiles = T64;
     }
+    // Under 4 workgroups of 64 x 64 per CU: the model's split, if any.
+    int64_t model_S = 1;
+    if (requested <= 0 && vec && (cfg == K4_T64 || cfg == K4_T64_WK4) && T64 < 4 * kCUs) {
+        model_S = t64_model_splits(g, T64, cfg == K4_T64_WK4);
+        if (model_S > 1) cfg = K4_T64;
+    }
     int64_t S = requested;
     if (S <= 0) {
-        S = 1;
+        S = model_S;
         if (cfg == K4_T32_WK4) {
             S = std::min<int64_t>(std::min(ceil_div(512, tiles), g.K / 256), 32);
             if (S >= 2 && g.K - ceil_div(g.K, S) < 512) S = 1;
@@ -651,18 +701,24 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     if (pack_b) gp.ldb = packed_ld(b_run);
     if (!k4_supports(gp)) return hipSuccess;
     if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512) return hipSuccess;
+    // The plan depends on the copies' addresses only through their 16-byte
+    // alignment, which the workspace layout below gives.
     const SplitPlan p = k4_plan(gp, 0);
-    if (p.splits > 1 || (p.cfg != K4_T64 && p.cfg != K4_T128 && p.cfg != K4_T128X256))
-        return hipSuccess;
-    // B's copy starts on a 256-byte boundary after A's.
+    if (p.cfg != K4_T64 && p.cfg != K4_T128 && p.cfg != K4_T128X256) return hipSuccess;
+    // Workspace: A's copy, B's copy, then the split's partial products,
+    // each on a 256-byte boundary.
     const size_t a_bytes = (size_t(a_floats) * sizeof(float) + 255) / 256 * 256;
+    const size_t b_bytes = (size_t(b_floats) * sizeof(float) + 255) / 256 * 256;
+    const size_t p_bytes = p.splits > 1 ? size_t(p.ws_floats) * sizeof(float) : 0;
     Workspace ws;
-    if (workspace_acquire(a_bytes + size_t(b_floats) * sizeof(float), s, &ws) != hipSuccess) {
+    if (workspace_acquire(a_bytes + b_bytes + p_bytes, s, &ws) != hipSuccess) {
         (void)hipGetLastError();
         return hipSuccess;  // no workspace: the 4-byte path
     }
     float* pa = static_cast<float*>(ws.ptr);
     float* pb = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes);
+    float* pp = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes + b_bytes)
+                             : nullptr;
     // One launch packs both operands when both need it.
     hipError_t e;
     if (pack_a && pack_b)
@@ -673,7 +729,7 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
         e = launch_pack(g.B, b_rows, b_run, g.ldb, pb, nullptr, 0, 0, 0, nullptr, s);
     if (pack_a) gp.A = pa;
     if (pack_b) gp.B = pb;
-    if (e == hipSuccess) e = launch_plan(gp, k4_plan(gp, 0), nullptr, s);
+    if (e == hipSuccess) e = launch_plan(gp, p, pp, s);
     const hipError_t f = workspace_release(&ws, s);
     *done = true;
     return e != hipSuccess ? e : f;

@@ -216,8 +216,9 @@ def test_split_plan_chunks_cover_k(lib, M, N, K, trans):
 
 
 def test_split_plan_choices(lib):
-    # Outputs of few 32 x 32 tiles with a long K are split; outputs of 64 x 64
-    # tiles or larger are not (measured: within noise or slower there).
+    # Outputs of few 32 x 32 tiles with a long K are split; outputs of fewer
+    # than 1024 64 x 64 tiles take the cost model's split when it saves 5 %;
+    # larger outputs are not split.
     plan = lambda M, N, K: rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)[0]
     assert plan(64, 64, 65536) == 32
     assert plan(128, 128, 4096) == 16
@@ -235,3 +236,22 @@ def test_split_plan_choices(lib):
     assert plan(3001, 4099, 2047) == 1
     # A short K is never cut below one slab.
     assert plan(64, 64, 40) == 1
+    # 64 x 64 tiles under 4 per CU with a long K (measured on MI355X against
+    # the unsplit choice: 64 x 8192 x 8192 153 -> 80 us, 192 x 8192 x 8192
+    # 297 -> 222, 1536^2 x 4096 214 -> 170, 256 x 2048 x 16384 304 -> 148).
+    assert plan(64, 8192, 8192) == 8
+    assert plan(8192, 64, 8192) == 8
+    assert plan(192, 8192, 8192) == 4
+    assert plan(1536, 1536, 4096) == 4
+    assert plan(256, 2048, 16384) == 8
+    assert plan(1536, 1024, 1024) == 2
+    # ... and where the model finds no 5 % (measured within noise).
+    assert plan(1024, 1024, 2048) == 1
+    assert plan(1280, 1280, 1280) == 1
+    assert plan(2048, 1024, 8192) == 1
+    assert plan(64, 16384, 4096) == 1
+    # No chunk below 512 of K from the model.
+    assert plan(768, 768, 768) == 1
+    for M, N, K in [(64, 8192, 1024), (768, 768, 4096), (512, 1024, 8192)]:
+        S, kc = rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
+        assert S > 1 and kc >= 512 and kc % 32 == 0 and (S - 1) * kc < K <= S * kc

@@ -203,3 +203,16 @@ def test_ex_packed_operands(ta, tb, shape):
     got, ref, S, E = run_ex(ta, tb, M, N, K, 1.5, 0.5, "uniform", seed=N + K, pad=1)
     rep = check.check_ex(got, ref, S, E, K)
     assert rep["ok"], rep
+
+
+def test_ex_packed_and_split():
+    # Unaligned operands whose packed copies get a split plan (600 tiles of
+    # 64 x 64, under 4 per CU, K = 4095): packing and split share one
+    # workspace.
+    M, N, K = 1535, 1537, 4095
+    print(f"[packed+split] {M}x{N}x{K}", flush=True)
+    got, ref, _, _ = run_ex(0, 0, M, N, K, 2.0, -1.0, "int", seed=5)
+    assert np.array_equal(got.astype(np.float64), ref)
+    got, ref, S, E = run_ex(0, 0, M, N, K, 1.0, 0.0, "uniform", seed=6)
+    rep = check.check_ex(got, ref, S, E, K)
+    assert rep["ok"], rep

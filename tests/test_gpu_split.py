@@ -121,7 +121,9 @@ def test_split_one_is_the_unsplit_kernel():
 # Shapes the shape-chosen plan splits, at full size through the plain entry
 # point sgemm_f32 (AUTO): every element against the oracle.
 AUTO_SPLIT = [(256, 256, 768, 3), (128, 128, 1024, 4), (128, 128, 4096, 16), (256, 256, 16384, 8),
-              (256, 256, 2048, 8), (64, 64, 65536, 32), (512, 512, 4096, 2), (200, 120, 3000, 0)]
+              (256, 256, 2048, 8), (64, 64, 65536, 32), (512, 512, 4096, 2), (200, 120, 3000, 0),
+              # 64 x 64 tiles split by the cost model
+              (64, 8192, 8192, 8), (192, 8192, 8192, 4), (1536, 1024, 1024, 2), (768, 768, 4096, 7)]
 
 
 @pytest.mark.parametrize("M,N,K,want", AUTO_SPLIT, ids=lambda v: str(v))
