@@ -41,9 +41,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(files=("k4_mfma.hip", "k4_layout.h")) -> str:
-    """Hash of the matrix-core kernel's code (comments and blank lines
-    dropped, so that editing a comment keeps recorded counters valid)."""
+def kernel_source_hash(files=("k4_mfma.hip", "k4_layout.h", "k4_plan.hip")) -> str:
+    """Hash of the matrix-core kernel's code and of the plan that picks its
+    configuration (comments and blank lines dropped, so that editing a
+    comment keeps recorded counters valid)."""
     import re
     h = hashlib.sha256()
     for f in files:

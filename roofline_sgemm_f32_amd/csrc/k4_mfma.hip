@@ -29,6 +29,8 @@
 //  * options for small outputs: K groups inside the workgroup (WK) and a
 //    split-K mode across workgroups (SPLITK, with a second reduction kernel);
 //    for the largest tiles, raised wave priority during the MFMAs (PRIO).
+// This file holds the kernel and one launcher per tile configuration; which
+// configuration and split a product gets is decided in k4_plan.hip.
 #include <algorithm>
 
 #include "k4_layout.h"
@@ -479,11 +481,11 @@ bool k4_supports(const GemmArgs& g) {
 
 // Whether an operand's rows suit 16-byte loads along its run (the stored
 // row length): aligned rows, and a run in whole 4-float chunks.
-static bool rows_vec(const float* p, int64_t ld, int64_t run) {
+bool rows_vec(const float* p, int64_t ld, int64_t run) {
     return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && run % 4 == 0;
 }
 
-static bool vec_ok(const GemmArgs& g) {
+bool vec_ok(const GemmArgs& g) {
     // 16-byte loads run along each operand's contiguous dimension; with
     // padded runs a chunk may straddle the run's end into the zero padding.
     const int64_t a_run = g.trans_a ? g.M : g.K, b_run = g.trans_b ? g.K : g.N;
@@ -491,41 +493,6 @@ static bool vec_ok(const GemmArgs& g) {
     const int64_t rb = g.runs_padded ? packed_ld(b_run) : b_run;
     return rows_vec(g.A, g.lda, ra) && rows_vec(g.B, g.ldb, rb);
 }
-
-// Tile configurations, chosen from sweeps on MI355X (square 256..8192,
-// K-heavy 64^2 x 65536 .. 1024^2 x 4096, skinny and unaligned shapes; every
-// sweep row checked bit-exact against a reference on integer data):
-//  * T128: 128 x 128 tiles, 4 waves of 2 x 2 accumulators, K slabs of 16,
-//    4 waves per SIMD: with at least two rounds of 1024 tiles (4 per CU) or
-//    whole rounds (square 6144: 3.34 ms against 3.62 on 64 x 64; 7168: 5.56
-//    against 5.72), and for transposed operands at square 4096;
-//  * T64: 64 x 64 tiles, 4 waves of 1 accumulator, K slabs of 32 with
-//    16-byte loads (fragments read in two halves: 7 % on square 1024), of 16
-//    with 4-byte loads: from 512 tiles up (more than 256 with 16-byte loads
-//    and more than 256 tiles of 32 x 32), when the larger tiles would leave
-//    a partial round (square 3072 0.488 ms against 0.575 on 128 x 128; 4608
-//    1.60 against 1.68; 5120 2.11 against 2.17; 3001 x 4099 x 2047);
-//  * T64_WK4: the same tile with 4 K groups (16 waves, one workgroup per CU
-//    by LDS): up to 256 such tiles with 16-byte loads (square 1024: 23.9 us
-//    against 24.2; 1024^2 x 4096: 79.8 against 86.9).  Between 256 and 512
-//    tiles a second round of these workgroups costs more than the groups
-//    save, and plain 64 x 64 tiles win (1536 x 1024 x 1024: 40.2 us against
-//    45.3; 1280^3: 49.3 against 54.7; 1408^2 x 2048: 76.5 against 83.0);
-//  * T32_WK4: 32 x 32 tiles, one wave per K group, 4 groups: outputs of at
-//    most 256 such tiles (square 256: 5.0 us against 7.9; square 512: 6.9
-//    against 13.2), and with 4-byte loads below 512 tiles of 64 x 64 as well
-//    (1024 x 1027 x 1024: 41.5 against 52.0).  A wave's chain of dependent
-//    matrix instructions is what bounds these shapes: 32 x 32 tiles give more
-//    workgroups, K groups shorten each chain.
-//  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
-//    SIMD, fragments read in halves, raised wave priority during the
-//    matrix instructions) for A and B as stored (no transposes) when the
-//    tiles fill whole rounds of 2 per CU, or the last round at least 3/4:
-//    square 4096 0.956 ms against 0.990 on 128 x 128, 8192 7.57 against
-//    7.79 ms, 5632 2.63 against 2.71; with a smaller last round (square
-//    3072, 4608, 6144) it is the slowest of the three, and with B stored
-//    transposed 128 x 128 is as fast.
-enum K4Cfg { K4_T128, K4_T64, K4_T64_WK4, K4_T32_WK4, K4_T128X256 };
 
 hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s) {
     using k4::Cfg;
@@ -539,14 +506,14 @@ hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
     return launch_k4_orient<2, 2, 2, 2, 16, false, 3, false, 2, 1, false>(g, s);
 }
 
-static hipError_t launch_k4_t64(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws) {
+hipError_t launch_k4_t64(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws) {
     if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s, splits, kchunk, ws);
     return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, splits, kchunk, ws);
 }
 
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) { return launch_k4_t64(g, s, 1, 0, nullptr); }
 
-static hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
+hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
                                     float* ws) {
     // Occupancy targets as the LDS allows them (2 and 4 workgroups per CU).
     if (vec_ok(g)) return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4>(g, s, splits, kchunk, ws);
@@ -555,220 +522,10 @@ static hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits
 
 // 16-byte loads only (the plan never picks it otherwise: with 4-byte loads
 // 64 x 64 tiles with K groups measured slower than 32 x 32 ones).
-static hipError_t launch_k4_t64_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
+hipError_t launch_k4_t64_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
                                     float* ws) {
     if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true, 2, 4>(g, s, splits, kchunk, ws);
     return launch_k4_t32_wk4(g, s, splits, kchunk, ws);
-}
-
-// Split-K on top of the tile choice, when the tiles alone leave the chip
-// underused (same sweeps, timed as back-to-back calls so that the second
-// launch, about 2.5 us, counts).
-//  * 32 x 32 tiles with K groups: with T tiles, up to ceil(512 / T) splits,
-//    each keeping at least 256 of K, and only when a workgroup's share of K
-//    shrinks by at least 512 (64^2 x 65536: 1316 us unsplit on 64 x 64
-//    tiles, 28 us on 32 x 32 with 32 splits; 128^2 x 4096: 85 -> 11.6 us;
-//    256^2 x 16384: 333 -> 32 us; 256^2 x 2048: 44 -> 11 us).
-//  * 64 x 64 tiles (16-byte loads, fewer than 1024 tiles, i.e. under 4 per
-//    CU): the split count from a cost model, below, when it saves at least
-//    5 % over the unsplit choice.  At most 16 splits of at least 512 of K.
-// Chunks are whole slabs.
-namespace {
-constexpr int kCUs = 256;
-// Sustained rate of one CU running n = 1..4 of the 64 x 64 workgroups, and
-// of one CU running the 4-K-group 64 x 64 workgroup, in FLOP per us; fixed
-// cost of a launch, and the split reduction's launch and bandwidth (bytes
-// per us).  Fitted to sweeps of 64..2048 x 64..16384 x 1024..16384 outputs
-// on MI355X (mean error 2 %).
-constexpr double kRate64[5] = {0.0, 0.405e6, 0.462e6, 0.475e6, 0.487e6};
-constexpr double kRate64Wk4 = 0.43e6;
-constexpr double kLaunchUs = 4.0, kReduceUs = 2.5, kReduceBytesPerUs = 5e6;
-
-// Estimated time of T 64 x 64 tiles over S chunks of kc of K: each CU runs
-// c = ceil(T S / 256) workgroups one after another at the rate c of them
-// sustain together, plus the reduction (S partial products read, C written).
-double t64_time_us(const GemmArgs& g, int64_t T, int64_t kc, int64_t S) {
-    const int64_t c = ceil_div(T * S, kCUs);
-    double t = kLaunchUs + double(c) * double(kc) * 8192.0 / kRate64[c < 4 ? c : 4];
-    if (S > 1) t += kReduceUs + 4.0 * double(g.M) * double(g.N) * double(S + 1) / kReduceBytesPerUs;
-    return t;
-}
-
-// Chunk count for 64 x 64 tiles by the model (1: no split pays).  wk4: the
-// unsplit choice is the 4-K-group workgroup (one per CU) rather than plain
-// 64 x 64 tiles.
-int64_t t64_model_splits(const GemmArgs& g, int64_t T, bool wk4) {
-    const double base = wk4 ? kLaunchUs + double(g.K) * 8192.0 / kRate64Wk4 : t64_time_us(g, T, g.K, 1);
-    double best = 0.95 * base;
-    int64_t pick = 1;
-    for (int64_t s = 2; s <= 16; s++) {
-        const int64_t kc = ceil_div(ceil_div(g.K, s), 32) * 32;
-        if (kc < 512) break;
-        const int64_t se = ceil_div(g.K, kc);
-        const double t = t64_time_us(g, T, kc, se);
-        if (t < best) {
-            best = t;
-            pick = se;
-        }
-    }
-    return pick;
-}
-}  // namespace
-
-SplitPlan k4_plan(const GemmArgs& g, int requested) {
-    const bool vec = vec_ok(g);
-    const int64_t bk = vec ? 32 : 16;
-    const int64_t T128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
-    const int64_t T64 = ceil_div(g.M, 64) * ceil_div(g.N, 64);
-    const int64_t T32 = ceil_div(g.M, 32) * ceil_div(g.N, 32);
-    const int64_t T256 = ceil_div(g.M, 128) * ceil_div(g.N, 256);
-    int cfg;
-    int64_t tiles;
-    // Large tiles pay off only when the workgroups fill their rounds: a
-    // partial last round of 128 x 256 (2 per CU) costs about a full one, of
-    // 128 x 128 (4 per CU) about its share.
-    if (vec && !g.trans_a && !g.trans_b && T256 >= 512 && (T256 % 512 == 0 || T256 % 512 >= 384)) {
-        cfg = K4_T128X256;
-        tiles = T256;
-    } else if (vec && (T128 >= 2048 || (T128 >= 1024 && T128 % 1024 == 0))) {
-        cfg = K4_T128;
-        tiles = T128;
-    } else if (T64 >= 512 || (vec && T64 > 256 && T32 > 256)) {
-        cfg = K4_T64;
-        tiles = T64;
-    } else if (T32 <= 256 || !vec) {
-        cfg = K4_T32_WK4;
-        tiles = T32;
-    } else {
-        cfg = K4_T64_WK4;
-        tiles = T64;
-    }
-    // Under 4 workgroups of 64 x 64 per CU: the model's split, if any.
-    int64_t model_S = 1;
-    if (requested <= 0 && vec && (cfg == K4_T64 || cfg == K4_T64_WK4) && T64 < 4 * kCUs) {
-        model_S = t64_model_splits(g, T64, cfg == K4_T64_WK4);
-        if (model_S > 1) cfg = K4_T64;
-    }
-    int64_t S = requested;
-    if (S <= 0) {
-        S = model_S;
-        if (cfg == K4_T32_WK4) {
-            S = std::min<int64_t>(std::min(ceil_div(512, tiles), g.K / 256), 32);
-            if (S >= 2 && g.K - ceil_div(g.K, S) < 512) S = 1;
-        }
-    }
-    // 128 x 128 and 128 x 256 tiles have no split variant: a requested split
-    // runs on 64 x 64.
-    if (S > 1 && (cfg == K4_T128 || cfg == K4_T128X256)) cfg = K4_T64;
-    S = std::min(S, ceil_div(g.K, bk));
-    if (S <= 1) return {1, g.K, 0, cfg};
-    const int64_t kc = ceil_div(ceil_div(g.K, S), bk) * bk;
-    S = ceil_div(g.K, kc);
-    return {(int)S, kc, S * g.M * g.N, cfg};
-}
-
-static hipError_t launch_plan(const GemmArgs& g, const SplitPlan& p, float* ws, hipStream_t s) {
-    const int kc = (int)p.kchunk;
-    switch (p.cfg) {
-        case K4_T128: return launch_k4_tile128(g, s);
-        case K4_T128X256: return launch_k4_tile128x256(g, s);
-        case K4_T64_WK4: return launch_k4_t64_wk4(g, s, p.splits, kc, ws);
-        case K4_T32_WK4: return launch_k4_t32_wk4(g, s, p.splits, kc, ws);
-        default: return launch_k4_t64(g, s, p.splits, kc, ws);
-    }
-}
-
-// Packing pre-pass: operands that do not suit 16-byte loads are copied into
-// zero-padded aligned rows (pack.hip) when the output is large enough for a
-// 64 x 64 or larger tile configuration, where the 16-byte path pays for the
-// copy (3001 x 4099 x 2047: 0.488 ms on 4-byte loads, 0.437 ms + 0.02 ms of
-// packing on 16-byte ones; 4095 x 4097 x 4093: 1.295 -> 1.158 + 0.04 ms).
-// Smaller outputs keep 4-byte loads.
-static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
-    *done = false;
-    if (vec_ok(g)) return hipSuccess;
-    GemmArgs gp = g;
-    gp.runs_padded = true;
-    const int64_t a_rows = g.trans_a ? g.K : g.M, a_run = g.trans_a ? g.M : g.K;
-    const int64_t b_rows = g.trans_b ? g.N : g.K, b_run = g.trans_b ? g.K : g.N;
-    const bool pack_a = !rows_vec(g.A, g.lda, a_run), pack_b = !rows_vec(g.B, g.ldb, b_run);
-    const int64_t a_floats = pack_a ? a_rows * packed_ld(a_run) : 0;
-    const int64_t b_floats = pack_b ? b_rows * packed_ld(b_run) : 0;
-    // Plan as if packed (16-byte loads); the pass is kept for large tiles only.
-    gp.A = pack_a ? reinterpret_cast<const float*>(uintptr_t(256)) : g.A;
-    gp.B = pack_b ? reinterpret_cast<const float*>(uintptr_t(256)) : g.B;
-    if (pack_a) gp.lda = packed_ld(a_run);
-    if (pack_b) gp.ldb = packed_ld(b_run);
-    if (!k4_supports(gp)) return hipSuccess;
-    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512) return hipSuccess;
-    // The plan depends on the copies' addresses only through their 16-byte
-    // alignment, which the workspace layout below gives.
-    const SplitPlan p = k4_plan(gp, 0);
-    if (p.cfg != K4_T64 && p.cfg != K4_T128 && p.cfg != K4_T128X256) return hipSuccess;
-    // Workspace: A's copy, B's copy, then the split's partial products,
-    // each on a 256-byte boundary.
-    const size_t a_bytes = (size_t(a_floats) * sizeof(float) + 255) / 256 * 256;
-    const size_t b_bytes = (size_t(b_floats) * sizeof(float) + 255) / 256 * 256;
-    const size_t p_bytes = p.splits > 1 ? size_t(p.ws_floats) * sizeof(float) : 0;
-    Workspace ws;
-    if (workspace_acquire(a_bytes + b_bytes + p_bytes, s, &ws) != hipSuccess) {
-        (void)hipGetLastError();
-        return hipSuccess;  // no workspace: the 4-byte path
-    }
-    float* pa = static_cast<float*>(ws.ptr);
-    float* pb = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes);
-    float* pp = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes + b_bytes)
-                             : nullptr;
-    // One launch packs both operands when both need it.
-    hipError_t e;
-    if (pack_a && pack_b)
-        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, g.B, b_rows, b_run, g.ldb, pb, s);
-    else if (pack_a)
-        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, nullptr, 0, 0, 0, nullptr, s);
-    else
-        e = launch_pack(g.B, b_rows, b_run, g.ldb, pb, nullptr, 0, 0, 0, nullptr, s);
-    if (pack_a) gp.A = pa;
-    if (pack_b) gp.B = pb;
-    if (e == hipSuccess) e = launch_plan(gp, p, pp, s);
-    const hipError_t f = workspace_release(&ws, s);
-    *done = true;
-    return e != hipSuccess ? e : f;
-}
-
-// Whether work on s is being captured into a graph.  The workspace paths
-// (split-K, packing) allocate stream-ordered memory and order uses across
-// streams with an event, which a capture cannot take part in; captured
-// calls run the unsplit kernel on the operands as stored instead, so every
-// entry point can be captured.
-static bool capturing(hipStream_t s) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    return st != hipStreamCaptureStatusNone;
-}
-
-hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
-    const bool in_graph = capturing(s);
-    if (requested == 0 && !in_graph) {
-        bool done;
-        const hipError_t e = launch_packed(g, s, &done);
-        if (done || e != hipSuccess) return e;
-    }
-    SplitPlan p = k4_plan(g, requested);
-    if (in_graph) p.splits = 1;
-    if (p.splits <= 1) return launch_plan(g, p, nullptr, s);
-    Workspace ws;
-    if (workspace_acquire(size_t(p.ws_floats) * sizeof(float), s, &ws) != hipSuccess) {
-        // No workspace: the unsplit kernel gives the same product.
-        (void)hipGetLastError();
-        p.splits = 1;
-        return launch_plan(g, p, nullptr, s);
-    }
-    const hipError_t e = launch_plan(g, p, static_cast<float*>(ws.ptr), s);
-    const hipError_t f = workspace_release(&ws, s);
-    return e != hipSuccess ? e : f;
 }
 
 }  // namespace sgemm

@@ -66,12 +66,25 @@ struct Workspace {
 };
 hipError_t workspace_acquire(size_t bytes, hipStream_t s, Workspace* ws);
 hipError_t workspace_release(Workspace* ws, hipStream_t s);
+// Tile configurations of the matrix-core kernel (k4_mfma.hip), as the plan
+// (k4_plan.hip) names them: 128 x 128, 64 x 64, 64 x 64 with 4 K groups,
+// 32 x 32 with 4 K groups, 128 x 256.
+enum K4Cfg { K4_T128, K4_T64, K4_T64_WK4, K4_T32_WK4, K4_T128X256 };
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s);
 // 128 x 256 tiles for A and B as stored (transposed operands: 128 x 128).
 hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s);
+// The configurations with a split-K mode: splits > 1 runs `splits` chunks of
+// kchunk of K into ws (splits * M * N floats), then the reduction into C.
+hipError_t launch_k4_t64(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws);
+hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws);
+hipError_t launch_k4_t64_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws);
 // Whether the matrix-core kernel's 32-bit buffer offsets can address this shape.
 bool k4_supports(const GemmArgs& g);
+// Whether rows of `run` floats at stride ld from p suit 16-byte loads
+// (aligned rows, whole 4-float chunks), and whether both operands do.
+bool rows_vec(const float* p, int64_t ld, int64_t run);
+bool vec_ok(const GemmArgs& g);
 hipError_t launch_zero(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 // C = beta * C (zeros when beta == 0, C then not read).
 hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta, hipStream_t s);
