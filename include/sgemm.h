@@ -154,6 +154,24 @@ int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K,
                      const float *A, int64_t lda, const float *B, int64_t ldb,
                      int splits, int64_t *kchunk);
 
+/* The matrix-core configuration a shape-chosen call (sgemm_f32, sgemm_f32_ex,
+ * or sgemm_f32_ex_split with splits == 0, not under graph capture) runs for
+ * these operands: host-only, no HIP call; the pointers enter only through
+ * their alignment.  Writes the workgroup's C tile (*tile_m x *tile_n), the
+ * number of K groups inside one workgroup (*k_groups), whether the operands
+ * are first copied into zero-padded aligned rows (*packed, 1 or 0) and the
+ * K chunk length (*kchunk); any of these pointers may be NULL.  Returns the
+ * number of K chunks (1 = unsplit); 0, with the outputs zero, when the call
+ * launches no matrix-core kernel (an empty product, K == 0, or a shape only
+ * the 64-bit kernel can address); or minus the status code of invalid flags,
+ * sizes or leading dimensions (C's leading dimension taken as max(1, N)).
+ * The tile sizes are among 128 x 256, 128 x 128, 64 x 64 and 32 x 32; which
+ * one a shape gets follows measurements on MI355X and may change between
+ * library versions. */
+int sgemm_plan_config(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                      const float *A, int64_t lda, const float *B, int64_t ldb,
+                      int *tile_m, int *tile_n, int *k_groups, int *packed, int64_t *kchunk);
+
 /* The same operation in column-major storage (the BLAS and cuBLAS
  * convention): C (m x n, ldc >= max(1, m)) = alpha * op(A) op(B) + beta * C,
  * op(A) m x k, op(B) k x n; A is m x k (lda >= max(1, m)) or, transposed,

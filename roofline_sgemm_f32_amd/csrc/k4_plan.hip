@@ -108,11 +108,19 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     int64_t tiles;
     // Large tiles pay off only when the workgroups fill their rounds: a
     // partial last round of 128 x 256 (2 per CU) costs about a full one, of
-    // 128 x 128 (4 per CU) about its share.
-    if (vec && !g.trans_a && !g.trans_b && T256 >= 512 && (T256 % 512 == 0 || T256 % 512 >= 384)) {
+    // 128 x 128 (4 per CU) about its share.  They must also be mostly full
+    // themselves (at least 7/8 of the tiles' area inside C): an edge tile
+    // does a whole tile's matrix work, so a narrow output wastes most of it
+    // (65536 x 128 x 1024: 251 us on 128 x 256, 156 on 64 x 64; 65536 x 64 x
+    // 4096: 961 against 335; 32768 x 320 x 2048: 485 against 360).
+    const double area = double(g.M) * double(g.N);
+    const bool full256 = area >= 0.875 * double(T256) * 128.0 * 256.0;
+    const bool full128 = area >= 0.875 * double(T128) * 128.0 * 128.0;
+    if (vec && !g.trans_a && !g.trans_b && full256 && T256 >= 512 &&
+        (T256 % 512 == 0 || T256 % 512 >= 384)) {
         cfg = K4_T128X256;
         tiles = T256;
-    } else if (vec && (T128 >= 2048 || (T128 >= 1024 && T128 % 1024 == 0))) {
+    } else if (vec && full128 && (T128 >= 2048 || (T128 >= 1024 && T128 % 1024 == 0))) {
         cfg = K4_T128;
         tiles = T128;
     } else if (T64 >= 512 || (vec && T64 > 256 && T32 > 256)) {
@@ -166,52 +174,82 @@ static hipError_t launch_plan(const GemmArgs& g, const SplitPlan& p, float* ws, 
 // copy (3001 x 4099 x 2047: 0.488 ms on 4-byte loads, 0.437 ms + 0.02 ms of
 // packing on 16-byte ones; 4095 x 4097 x 4093: 1.295 -> 1.158 + 0.04 ms).
 // Smaller outputs keep 4-byte loads.
-static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
-    *done = false;
-    if (vec_ok(g)) return hipSuccess;
+namespace {
+struct PackPlan {
+    bool pack_a = false, pack_b = false;
+    int64_t a_rows = 0, a_run = 0, b_rows = 0, b_run = 0;
+    size_t a_bytes = 0, b_bytes = 0;  // each copy rounded up to 256 bytes
+    GemmArgs gp;                      // the product on the copies
+    SplitPlan p;                      // and its plan
+};
+}  // namespace
+
+// Whether an eager shape-chosen call packs g's operands first, and then how.
+// The plan depends on the copies' addresses only through their 16-byte
+// alignment, which the workspace layout gives; until the copies exist gp
+// holds an aligned placeholder address for them.
+static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
+    if (vec_ok(g)) return false;
+    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512) return false;
     GemmArgs gp = g;
     gp.runs_padded = true;
-    const int64_t a_rows = g.trans_a ? g.K : g.M, a_run = g.trans_a ? g.M : g.K;
-    const int64_t b_rows = g.trans_b ? g.N : g.K, b_run = g.trans_b ? g.K : g.N;
-    const bool pack_a = !rows_vec(g.A, g.lda, a_run), pack_b = !rows_vec(g.B, g.ldb, b_run);
-    const int64_t a_floats = pack_a ? a_rows * packed_ld(a_run) : 0;
-    const int64_t b_floats = pack_b ? b_rows * packed_ld(b_run) : 0;
-    // Plan as if packed (16-byte loads); the pass is kept for large tiles only.
-    gp.A = pack_a ? reinterpret_cast<const float*>(uintptr_t(256)) : g.A;
-    gp.B = pack_b ? reinterpret_cast<const float*>(uintptr_t(256)) : g.B;
-    if (pack_a) gp.lda = packed_ld(a_run);
-    if (pack_b) gp.ldb = packed_ld(b_run);
-    if (!k4_supports(gp)) return hipSuccess;
-    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512) return hipSuccess;
-    // The plan depends on the copies' addresses only through their 16-byte
-    // alignment, which the workspace layout below gives.
-    const SplitPlan p = k4_plan(gp, 0);
-    if (p.cfg != K4_T64 && p.cfg != K4_T128 && p.cfg != K4_T128X256) return hipSuccess;
+    pk->a_rows = g.trans_a ? g.K : g.M;
+    pk->a_run = g.trans_a ? g.M : g.K;
+    pk->b_rows = g.trans_b ? g.N : g.K;
+    pk->b_run = g.trans_b ? g.K : g.N;
+    pk->pack_a = !rows_vec(g.A, g.lda, pk->a_run);
+    pk->pack_b = !rows_vec(g.B, g.ldb, pk->b_run);
+    if (pk->pack_a) {
+        gp.A = reinterpret_cast<const float*>(uintptr_t(256));
+        gp.lda = packed_ld(pk->a_run);
+        pk->a_bytes = (size_t(pk->a_rows * gp.lda) * sizeof(float) + 255) / 256 * 256;
+    }
+    if (pk->pack_b) {
+        gp.B = reinterpret_cast<const float*>(uintptr_t(256));
+        gp.ldb = packed_ld(pk->b_run);
+        pk->b_bytes = (size_t(pk->b_rows * gp.ldb) * sizeof(float) + 255) / 256 * 256;
+    }
+    if (!k4_supports(gp)) return false;
+    pk->p = k4_plan(gp, 0);
+    if (pk->p.cfg != K4_T64 && pk->p.cfg != K4_T128 && pk->p.cfg != K4_T128X256) return false;
+    pk->gp = gp;
+    return true;
+}
+
+SplitPlan k4_effective_plan(const GemmArgs& g, bool* packed) {
+    PackPlan pk;
+    *packed = packing_plan(g, &pk);
+    return *packed ? pk.p : k4_plan(g, 0);
+}
+
+static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
+    *done = false;
+    PackPlan pk;
+    if (!packing_plan(g, &pk)) return hipSuccess;
     // Workspace: A's copy, B's copy, then the split's partial products,
     // each on a 256-byte boundary.
-    const size_t a_bytes = (size_t(a_floats) * sizeof(float) + 255) / 256 * 256;
-    const size_t b_bytes = (size_t(b_floats) * sizeof(float) + 255) / 256 * 256;
-    const size_t p_bytes = p.splits > 1 ? size_t(p.ws_floats) * sizeof(float) : 0;
+    const size_t p_bytes = pk.p.splits > 1 ? size_t(pk.p.ws_floats) * sizeof(float) : 0;
     Workspace ws;
-    if (workspace_acquire(a_bytes + b_bytes + p_bytes, s, &ws) != hipSuccess) {
+    if (workspace_acquire(pk.a_bytes + pk.b_bytes + p_bytes, s, &ws) != hipSuccess) {
         (void)hipGetLastError();
         return hipSuccess;  // no workspace: the 4-byte path
     }
-    float* pa = static_cast<float*>(ws.ptr);
-    float* pb = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes);
-    float* pp = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + a_bytes + b_bytes)
-                             : nullptr;
+    char* base = static_cast<char*>(ws.ptr);
+    float* pa = reinterpret_cast<float*>(base);
+    float* pb = reinterpret_cast<float*>(base + pk.a_bytes);
+    float* pp = pk.p.splits > 1 ? reinterpret_cast<float*>(base + pk.a_bytes + pk.b_bytes) : nullptr;
     // One launch packs both operands when both need it.
     hipError_t e;
-    if (pack_a && pack_b)
-        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, g.B, b_rows, b_run, g.ldb, pb, s);
-    else if (pack_a)
-        e = launch_pack(g.A, a_rows, a_run, g.lda, pa, nullptr, 0, 0, 0, nullptr, s);
+    if (pk.pack_a && pk.pack_b)
+        e = launch_pack(g.A, pk.a_rows, pk.a_run, g.lda, pa, g.B, pk.b_rows, pk.b_run, g.ldb, pb, s);
+    else if (pk.pack_a)
+        e = launch_pack(g.A, pk.a_rows, pk.a_run, g.lda, pa, nullptr, 0, 0, 0, nullptr, s);
     else
-        e = launch_pack(g.B, b_rows, b_run, g.ldb, pb, nullptr, 0, 0, 0, nullptr, s);
-    if (pack_a) gp.A = pa;
-    if (pack_b) gp.B = pb;
-    if (e == hipSuccess) e = launch_plan(gp, p, pp, s);
+        e = launch_pack(g.B, pk.b_rows, pk.b_run, g.ldb, pb, nullptr, 0, 0, 0, nullptr, s);
+    GemmArgs gp = pk.gp;
+    if (pk.pack_a) gp.A = pa;
+    if (pk.pack_b) gp.B = pb;
+    if (e == hipSuccess) e = launch_plan(gp, pk.p, pp, s);
     const hipError_t f = workspace_release(&ws, s);
     *done = true;
     return e != hipSuccess ? e : f;

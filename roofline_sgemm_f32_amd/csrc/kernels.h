@@ -55,6 +55,9 @@ struct SplitPlan {
 };
 // requested_splits 0: split by shape; > 0: at most that many chunks.
 SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
+// The plan an eager shape-chosen call runs: that of the packed copies when
+// the packing pre-pass applies (*packed), else k4_plan(g, 0).
+SplitPlan k4_effective_plan(const GemmArgs& g, bool* packed);
 // Scratch memory for launches that need it: the device's cached buffer,
 // held (with the device's workspace lock) from acquire to release; every
 // launch that uses it goes on stream s in between.

@@ -255,3 +255,46 @@ def test_split_plan_choices(lib):
     for M, N, K in [(64, 8192, 1024), (768, 768, 4096), (512, 1024, 8192)]:
         S, kc = rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
         assert S > 1 and kc >= 512 and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
+
+
+def test_plan_config_choices(lib):
+    # Tile configuration of shape-chosen calls (measured choices on MI355X).
+    cfg = lambda M, N, K, **kw: rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED, **kw)
+    big = cfg(4096, 4096, 4096)
+    assert big == {"tile": (128, 256), "k_groups": 1, "packed": False, "splits": 1, "kchunk": 4096}
+    assert cfg(8192, 8192, 8192)["tile"] == (128, 256)
+    assert cfg(4096, 4096, 4096, transb=True)["tile"] == (128, 128)   # 128 x 256 needs A, B as stored
+    assert cfg(6144, 6144, 6144)["tile"] == (128, 128)               # 2.25 rounds of 128 x 256
+    assert cfg(3072, 3072, 3072)["tile"] == (64, 64)
+    assert cfg(1024, 1024, 1024)["tile"] == (64, 64) and cfg(1024, 1024, 1024)["k_groups"] == 4
+    small = cfg(256, 256, 256)
+    assert small["tile"] == (32, 32) and small["k_groups"] == 4 and small["splits"] == 1
+    assert cfg(128, 128, 4096)["splits"] == 16
+    skinny = cfg(64, 8192, 8192)
+    assert skinny["tile"] == (64, 64) and skinny["k_groups"] == 1 and skinny["splits"] == 8
+    # Narrow outputs: 128 x 256 and 128 x 128 tiles would be mostly empty.
+    for M, N, K in [(65536, 128, 1024), (65536, 64, 4096), (65536, 160, 2048), (65536, 192, 1024),
+                    (32768, 320, 2048)]:
+        assert cfg(M, N, K)["tile"] == (64, 64), (M, N, K)
+    # Unaligned operands of a large output: packed copies, 64 x 64 tiles.
+    ragged = cfg(3001, 4099, 2047)
+    assert ragged["packed"] and ragged["tile"] == (64, 64) and ragged["splits"] == 1
+
+
+def test_plan_config_agrees_with_split_plan(lib):
+    for M, N, K in [(64, 64, 65536), (256, 256, 768), (512, 512, 4096), (192, 8192, 8192),
+                    (1024, 1024, 4096), (4096, 4096, 4096), (1536, 1024, 1024)]:
+        c = rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
+        assert (c["splits"], c["kchunk"]) == rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
+
+
+def test_plan_config_empty_and_errors(lib):
+    for M, N, K in [(0, 5, 5), (5, 0, 5), (5, 5, 0)]:
+        c = rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
+        assert c == {"tile": (0, 0), "k_groups": 0, "packed": False, "splits": 0, "kchunk": 0}
+    with pytest.raises(rs.SgemmError):
+        rs.plan_config(-1, 4, 4)
+    with pytest.raises(rs.SgemmError):
+        rs.plan_config(64, 64, 64, lda=10)
+    assert lib.sgemm_plan_config(0, 0, 64, 64, 64, None, 64, None, 64, None, None, None, None,
+                                 None) == 1

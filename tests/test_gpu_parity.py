@@ -236,3 +236,17 @@ def test_workload_integer_exact(name):
     cols = _sample(w.N, 16, 4)
     ref, _ = oracle.sgemm_f64(An, np.ascontiguousarray(Bn[:, cols]), bound=False)
     assert np.array_equal(C[:, cols].astype(np.float64), ref)
+
+
+# Narrow outputs where the plan keeps 64 x 64 tiles (128 x 256 or 128 x 128
+# ones would be mostly empty), and an output split by the 64 x 64 cost model:
+# AUTO against the full oracle, uniform and integer operands.
+NARROW = [(65536, 64, 256), (16384, 160, 512), (8192, 320, 300), (192, 2048, 4096)]
+
+
+@pytest.mark.parametrize("shape", NARROW, ids=lambda s: "x".join(map(str, s)))
+def test_narrow_outputs_auto(shape):
+    M, N, K = shape
+    note(f"[narrow] {M}x{N}x{K} plan {rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)}")
+    full_check("auto", M, N, K, "uniform", seed=M + N)
+    full_check("auto", M, N, K, "int", seed=M + K)
