@@ -190,7 +190,6 @@ struct PackPlan {
 // holds an aligned placeholder address for them.
 static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
     if (vec_ok(g)) return false;
-    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512) return false;
     GemmArgs gp = g;
     gp.runs_padded = true;
     pk->a_rows = g.trans_a ? g.K : g.M;
@@ -210,8 +209,17 @@ static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
         pk->b_bytes = (size_t(pk->b_rows * gp.ldb) * sizeof(float) + 255) / 256 * 256;
     }
     if (!k4_supports(gp)) return false;
+    // Worth a copy launch: outputs of at least 512 tiles of 64 x 64; or a
+    // product moving 64 MB or more whose copies are at most 1/8 of that, as
+    // when a narrow or thin operand is the only unaligned one (8192 x 1 x
+    // 8192: 79 -> 60 us; 3 x 8192 x 8191: 79 -> 59).  Copying a large
+    // operand of a mid-size product did not pay (1024 x 1027 x 1024: 41.7
+    // -> 45.3 us; 1 x 8191 x 8192, B copied: 79 -> 144).
+    const double moved = 4.0 * (double(g.M) * g.K + double(g.K) * g.N + double(g.M) * g.N);
+    const double copied = double(pk->a_bytes + pk->b_bytes);
+    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512 && !(moved >= 64e6 && copied <= moved / 8))
+        return false;
     pk->p = k4_plan(gp, 0);
-    if (pk->p.cfg != K4_T64 && pk->p.cfg != K4_T128 && pk->p.cfg != K4_T128X256) return false;
     pk->gp = gp;
     return true;
 }

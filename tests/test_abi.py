@@ -279,6 +279,11 @@ def test_plan_config_choices(lib):
     # Unaligned operands of a large output: packed copies, 64 x 64 tiles.
     ragged = cfg(3001, 4099, 2047)
     assert ragged["packed"] and ragged["tile"] == (64, 64) and ragged["splits"] == 1
+    # A thin unaligned operand of a large product is copied; a large one of a
+    # memory-bound product, or the operands of a mid-size product, are not.
+    assert cfg(8192, 1, 8192)["packed"] and cfg(3, 8192, 8191)["packed"]
+    assert not cfg(1, 8191, 8192)["packed"]
+    assert not cfg(1024, 1027, 1024)["packed"] and not cfg(1023, 1023, 1023)["packed"]
 
 
 def test_plan_config_agrees_with_split_plan(lib):

@@ -250,3 +250,19 @@ def test_narrow_outputs_auto(shape):
     note(f"[narrow] {M}x{N}x{K} plan {rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)}")
     full_check("auto", M, N, K, "uniform", seed=M + N)
     full_check("auto", M, N, K, "int", seed=M + K)
+
+
+# Thin unaligned operands of large products: the packing pre-pass copies the
+# thin one (B with 1 or 3 columns, A with K = 8191) and the product runs on
+# 16-byte loads with a K split, all through one workspace.
+THIN = [(8192, 1, 8192), (8192, 3, 4096), (3, 8192, 8191)]
+
+
+@pytest.mark.parametrize("shape", THIN, ids=lambda s: "x".join(map(str, s)))
+def test_thin_unaligned_auto(shape):
+    M, N, K = shape
+    plan = rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)
+    note(f"[thin] {M}x{N}x{K} plan {plan}")
+    assert plan["packed"]
+    full_check("auto", M, N, K, "uniform", seed=M + N)
+    full_check("auto", M, N, K, "int", seed=M + K)
