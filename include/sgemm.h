@@ -154,22 +154,26 @@ int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K,
                      const float *A, int64_t lda, const float *B, int64_t ldb,
                      int splits, int64_t *kchunk);
 
-/* The matrix-core configuration a shape-chosen call (sgemm_f32, sgemm_f32_ex,
- * or sgemm_f32_ex_split with splits == 0, not under graph capture) runs for
+/* The kernel configuration a shape-chosen call (sgemm_f32, sgemm_f32_ex, or
+ * sgemm_f32_ex_split with splits == 0, not under graph capture) runs for
  * these operands: host-only, no HIP call; the pointers enter only through
- * their alignment.  Writes the workgroup's C tile (*tile_m x *tile_n), the
- * number of K groups inside one workgroup (*k_groups), whether the operands
- * are first copied into zero-padded aligned rows (*packed, 1 or 0) and the
- * K chunk length (*kchunk); any of these pointers may be NULL.  Returns the
- * number of K chunks (1 = unsplit); 0, with the outputs zero, when the call
- * launches no matrix-core kernel (an empty product, K == 0, or a shape only
- * the 64-bit kernel can address); or minus the status code of invalid flags,
- * sizes or leading dimensions (C's leading dimension taken as max(1, N)).
- * The tile sizes are among 128 x 256, 128 x 128, 64 x 64 and 32 x 32; which
- * one a shape gets follows measurements on MI355X and may change between
- * library versions. */
+ * their alignment.  Writes the engine (*engine: 1 = the matrix-core kernel,
+ * 2 = the thin-product kernels on the vector units, for M <= 8 or N <= 8
+ * when the large operand suits 16-byte loads and is 384 MB or more, or 16 MB
+ * or more for N == 1), the
+ * workgroup's C tile (*tile_m x *tile_n), the number of K ranges one
+ * workgroup splits its work into (*k_groups), whether the operands are
+ * first copied into zero-padded aligned rows (*packed, 1 or 0) and the K
+ * chunk length (*kchunk); any of these pointers may be NULL.  Returns the
+ * number of K chunks across workgroups (1 = unsplit); 0, with the outputs
+ * zero, when the call launches neither (an empty product, K == 0, or a
+ * shape only the 64-bit kernel can address); or minus the status code of
+ * invalid flags, sizes or leading dimensions (C's leading dimension taken
+ * as max(1, N)).  Matrix-core tiles are among 128 x 256, 128 x 128, 64 x 64
+ * and 32 x 32; which configuration a shape gets follows measurements on
+ * MI355X and may change between library versions. */
 int sgemm_plan_config(int transa, int transb, int64_t M, int64_t N, int64_t K,
-                      const float *A, int64_t lda, const float *B, int64_t ldb,
+                      const float *A, int64_t lda, const float *B, int64_t ldb, int *engine,
                       int *tile_m, int *tile_n, int *k_groups, int *packed, int64_t *kchunk);
 
 /* The same operation in column-major storage (the BLAS and cuBLAS

@@ -86,7 +86,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_split_plan.restype = cint
     ip = ctypes.POINTER(cint)
     lib.sgemm_plan_config.argtypes = [cint, cint, i64, i64, i64, vp, i64, vp, i64, ip, ip, ip, ip,
-                                      ctypes.POINTER(i64)]
+                                      ip, ctypes.POINTER(i64)]
     lib.sgemm_plan_config.restype = cint
     lib.sgemm_copy_f32.argtypes = [vp, vp, i64, vp]
     lib.sgemm_copy_f32.restype = cint
@@ -222,20 +222,21 @@ def split_plan(M, N, K, transa=False, transb=False, lda=None, ldb=None, A_ptr=0,
 
 
 def plan_config(M, N, K, transa=False, transb=False, lda=None, ldb=None, A_ptr=0, B_ptr=0):
-    """The matrix-core configuration a shape-chosen call runs (host only):
-    dict with tile (tile_m, tile_n), k_groups, packed, splits, kchunk; splits
-    0 when no matrix-core kernel is launched."""
+    """The kernel configuration a shape-chosen call runs (host only): dict
+    with engine ("mfma", "thin" or None), tile (tile_m, tile_n), k_groups,
+    packed, splits, kchunk; splits 0 when neither kernel is launched."""
     lda = (max(M, 1) if transa else max(K, 1)) if lda is None else lda
     ldb = (max(K, 1) if transb else max(N, 1)) if ldb is None else ldb
-    tm, tn, wk, pk = (ctypes.c_int(0) for _ in range(4))
+    en, tm, tn, wk, pk = (ctypes.c_int(0) for _ in range(5))
     kc = ctypes.c_int64(0)
     r = load().sgemm_plan_config(int(transa), int(transb), M, N, K, A_ptr or None, lda,
-                                 B_ptr or None, ldb, ctypes.byref(tm), ctypes.byref(tn),
-                                 ctypes.byref(wk), ctypes.byref(pk), ctypes.byref(kc))
+                                 B_ptr or None, ldb, ctypes.byref(en), ctypes.byref(tm),
+                                 ctypes.byref(tn), ctypes.byref(wk), ctypes.byref(pk),
+                                 ctypes.byref(kc))
     if r < 0:
         raise SgemmError(-r, "sgemm_plan_config")
-    return {"tile": (tm.value, tn.value), "k_groups": wk.value, "packed": bool(pk.value),
-            "splits": r, "kchunk": kc.value}
+    return {"engine": {1: "mfma", 2: "thin"}.get(en.value), "tile": (tm.value, tn.value),
+            "k_groups": wk.value, "packed": bool(pk.value), "splits": r, "kchunk": kc.value}
 
 
 def _ld_col(t, name):

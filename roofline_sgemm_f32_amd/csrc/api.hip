@@ -180,48 +180,31 @@ int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K, co
     GemmArgs g{M, N, K, A, lda, B, ldb, nullptr, N > 1 ? N : 1};
     g.trans_a = transa == SGEMM_OP_T;
     g.trans_b = transb == SGEMM_OP_T;
-    sgemm::SplitPlan p{1, K, 0, 0};
-    if (M > 0 && N > 0 && K > 0 && sgemm::k4_supports(g)) p = sgemm::k4_plan(g, splits);
+    sgemm::PlanInfo p;
+    p.splits = 1;
+    p.kchunk = K;
+    if (M > 0 && N > 0 && K > 0 && sgemm::k4_supports(g)) p = sgemm::plan_info(g, splits);
     if (kchunk) *kchunk = p.kchunk;
     return p.splits;
 }
 
 int sgemm_plan_config(int transa, int transb, int64_t M, int64_t N, int64_t K, const float* A,
-                      int64_t lda, const float* B, int64_t ldb, int* tile_m, int* tile_n,
-                      int* k_groups, int* packed, int64_t* kchunk) {
+                      int64_t lda, const float* B, int64_t ldb, int* engine, int* tile_m,
+                      int* tile_n, int* k_groups, int* packed, int64_t* kchunk) {
     const int v = validate_ex_shape(transa, transb, M, N, K, lda, ldb, N > 1 ? N : 1);
     if (v != SGEMM_OK) return -v;
     GemmArgs g{M, N, K, A, lda, B, ldb, nullptr, N > 1 ? N : 1};
     g.trans_a = transa == SGEMM_OP_T;
     g.trans_b = transb == SGEMM_OP_T;
-    int tm = 0, tn = 0, wk = 0, pk = 0, splits = 0;
-    int64_t kc = 0;
-    if (M > 0 && N > 0 && K > 0 && sgemm::k4_supports(g)) {
-        bool was_packed = false;
-        const sgemm::SplitPlan p = sgemm::k4_effective_plan(g, &was_packed);
-        static_assert(sgemm::K4_T128 == 0 && sgemm::K4_T64 == 1 && sgemm::K4_T64_WK4 == 2 &&
-                          sgemm::K4_T32_WK4 == 3 && sgemm::K4_T128X256 == 4,
-                      "table order");
-        static const int dims[][3] = {
-            {128, 128, 1},  // K4_T128
-            {64, 64, 1},    // K4_T64
-            {64, 64, 4},    // K4_T64_WK4
-            {32, 32, 4},    // K4_T32_WK4
-            {128, 256, 1},  // K4_T128X256
-        };
-        tm = dims[p.cfg][0];
-        tn = dims[p.cfg][1];
-        wk = dims[p.cfg][2];
-        pk = was_packed ? 1 : 0;
-        splits = p.splits;
-        kc = p.kchunk;
-    }
-    if (tile_m) *tile_m = tm;
-    if (tile_n) *tile_n = tn;
-    if (k_groups) *k_groups = wk;
-    if (packed) *packed = pk;
-    if (kchunk) *kchunk = kc;
-    return splits;
+    sgemm::PlanInfo p;
+    if (M > 0 && N > 0 && K > 0 && sgemm::k4_supports(g)) p = sgemm::plan_info(g, 0);
+    if (engine) *engine = p.engine;
+    if (tile_m) *tile_m = p.tile_m;
+    if (tile_n) *tile_n = p.tile_n;
+    if (k_groups) *k_groups = p.k_groups;
+    if (packed) *packed = p.packed ? 1 : 0;
+    if (kchunk) *kchunk = p.kchunk;
+    return p.splits;
 }
 
 int sgemm_copy_f32_launch(float* dst, const float* src, int64_t n, int block, int64_t grid,

@@ -224,12 +224,6 @@ static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
     return true;
 }
 
-SplitPlan k4_effective_plan(const GemmArgs& g, bool* packed) {
-    PackPlan pk;
-    *packed = packing_plan(g, &pk);
-    return *packed ? pk.p : k4_plan(g, 0);
-}
-
 static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     *done = false;
     PackPlan pk;
@@ -263,6 +257,79 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     return e != hipSuccess ? e : f;
 }
 
+// Thin products (one side of C at most 8) stream their large operand on the
+// vector units (thin.hip) when it suits 16-byte loads (B stored K x N for
+// M <= 8, A stored M x K for N <= 8) and is 384 MB or more, or, for a single
+// column of C, 16 MB or more.  Measured against the matrix-core path, whose
+// 32 x 32 tiles stream the operand too (MI355X, back-to-back calls, us):
+// 1 x 16384 x 16384 290 -> 168, 16384 x 8 x 16384 296 -> 223, 2 x 65536 x
+// 4096 286 -> 174, 100000 x 4 x 1024 127 -> 80, 8192 x 1 x 8192 79 -> 68;
+// at 268 MB with more than one column the thin kernels were no faster (1 x
+// 8192 x 8192 55 -> 67, 8192 x 8 x 8192 56 -> 82): the fixed costs of the
+// split and of staging B weigh more there.  K is split so that about 1024
+// workgroups of 4 waves (4 per CU) keep loads in flight; a chunk keeps at
+// least 256 of K (thin_m) or one 1024-k piece (thin_n).
+ThinPlan thin_plan(const GemmArgs& g) {
+    ThinPlan t;
+    constexpr int64_t kTarget = 1024, kMinBytes = int64_t(384) << 20, kMinColumn = int64_t(16) << 20;
+    int64_t groups = 0, min_chunk = 0, quantum = 4;
+    if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes && rows_vec(g.B, g.ldb, g.N)) {
+        t.kind = ThinPlan::THIN_M;
+        groups = ceil_div(g.N, 256);
+        min_chunk = 256;
+    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= (g.N == 1 ? kMinColumn : kMinBytes) &&
+               rows_vec(g.A, g.lda, g.K)) {
+        t.kind = ThinPlan::THIN_N;
+        groups = ceil_div(g.M, 16);
+        min_chunk = 1024;
+        quantum = 1024;
+    } else {
+        return t;
+    }
+    int64_t S = std::min<int64_t>(std::min(ceil_div(kTarget, groups), g.K / min_chunk), 64);
+    if (S < 1) S = 1;
+    const int64_t kc = ceil_div(ceil_div(g.K, S), quantum) * quantum;
+    t.splits = (int)ceil_div(g.K, kc);
+    t.kchunk = t.splits > 1 ? kc : g.K;
+    t.ws_floats = t.splits > 1 ? t.splits * g.M * g.N : 0;
+    return t;
+}
+
+PlanInfo plan_info(const GemmArgs& g, int requested) {
+    PlanInfo info;
+    if (requested == 0) {
+        const ThinPlan t = thin_plan(g);
+        if (t.kind != ThinPlan::NONE) {
+            info.engine = 2;
+            info.tile_m = t.kind == ThinPlan::THIN_M ? (int)g.M : 16;
+            info.tile_n = t.kind == ThinPlan::THIN_M ? 256 : (int)g.N;
+            info.k_groups = t.kind == ThinPlan::THIN_M ? 4 : 1;
+            info.splits = t.splits;
+            info.kchunk = t.kchunk;
+            return info;
+        }
+    }
+    PackPlan pk;
+    info.packed = requested == 0 && packing_plan(g, &pk);
+    const SplitPlan p = info.packed ? pk.p : k4_plan(g, requested);
+    static const int dims[][3] = {
+        {128, 128, 1},  // K4_T128
+        {64, 64, 1},    // K4_T64
+        {64, 64, 4},    // K4_T64_WK4
+        {32, 32, 4},    // K4_T32_WK4
+        {128, 256, 1},  // K4_T128X256
+    };
+    static_assert(K4_T128 == 0 && K4_T64 == 1 && K4_T64_WK4 == 2 && K4_T32_WK4 == 3 && K4_T128X256 == 4,
+                  "table order");
+    info.engine = 1;
+    info.tile_m = dims[p.cfg][0];
+    info.tile_n = dims[p.cfg][1];
+    info.k_groups = dims[p.cfg][2];
+    info.splits = p.splits;
+    info.kchunk = p.kchunk;
+    return info;
+}
+
 // Whether work on s is being captured into a graph.  The workspace paths
 // (split-K, packing) allocate stream-ordered memory and order uses across
 // streams with an event, which a capture cannot take part in; captured
@@ -279,6 +346,23 @@ static bool capturing(hipStream_t s) {
 
 hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
     const bool in_graph = capturing(s);
+    if (requested == 0) {
+        ThinPlan t = thin_plan(g);
+        if (t.kind != ThinPlan::NONE) {
+            Workspace ws;
+            if (t.splits > 1 && (in_graph || workspace_acquire(size_t(t.ws_floats) * sizeof(float), s,
+                                                               &ws) != hipSuccess)) {
+                // Captured, or no workspace: one chunk gives the same product.
+                if (!in_graph) (void)hipGetLastError();
+                t.splits = 1;
+                t.kchunk = g.K;
+            }
+            const hipError_t e = launch_thin(g, t, static_cast<float*>(ws.ptr), s);
+            if (t.splits <= 1) return e;
+            const hipError_t f = workspace_release(&ws, s);
+            return e != hipSuccess ? e : f;
+        }
+    }
     if (requested == 0 && !in_graph) {
         bool done;
         const hipError_t e = launch_packed(g, s, &done);

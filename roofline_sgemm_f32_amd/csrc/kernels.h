@@ -55,9 +55,31 @@ struct SplitPlan {
 };
 // requested_splits 0: split by shape; > 0: at most that many chunks.
 SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
-// The plan an eager shape-chosen call runs: that of the packed copies when
-// the packing pre-pass applies (*packed), else k4_plan(g, 0).
-SplitPlan k4_effective_plan(const GemmArgs& g, bool* packed);
+// Thin products on the vector units (thin.hip): M <= 8 (B streamed) or
+// N <= 8 (A streamed), in `splits` K chunks of kchunk whose partial
+// products take ws_floats floats of workspace.
+struct ThinPlan {
+    enum Kind { NONE, THIN_M, THIN_N } kind = NONE;
+    int splits = 1;
+    int64_t kchunk = 0, ws_floats = 0;
+};
+// Whether a shape-chosen call takes the thin path, and how.
+ThinPlan thin_plan(const GemmArgs& g);
+// What an eager call with this K-split request runs (requested 0: shape-
+// chosen): engine 1 the matrix-core kernel, 2 the thin vector kernels; the
+// workgroup's C tile and K groups; whether operands are packed first; the
+// K chunks.
+struct PlanInfo {
+    int engine = 0, tile_m = 0, tile_n = 0, k_groups = 0;
+    bool packed = false;
+    int splits = 0;
+    int64_t kchunk = 0;
+};
+PlanInfo plan_info(const GemmArgs& g, int requested);
+hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStream_t s);
+// Split-K second pass: C = alpha * (sum of the `splits` dense M x N slabs of
+// ws, added in slab order) (+ beta * C).
+hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, hipStream_t s);
 // Scratch memory for launches that need it: the device's cached buffer,
 // held (with the device's workspace lock) from acquire to release; every
 // launch that uses it goes on stream s in between.

@@ -1,0 +1,250 @@
+// Thin products on the vector units: one dimension of C of at most 8.
+//
+// With M <= 8 (or N <= 8) the product reads the large operand once and does
+// at most 16 FLOP per 4-byte element of it, far under the MI355X ridge of
+// about 20 FLOP per byte, so the memory roof binds (amittech.dev, "7.3
+// Bandwidths and peak rate - exercises", exercises 4 and 6: a kernel's
+// intensity against the ridge decides which roof applies), and a 32 x 32
+// matrix-core tile would mostly multiply padding.  These kernels stream the
+// large operand in 16-byte loads along its contiguous dimension, one pass,
+// and keep the small one close:
+//  * thin_m (M <= 8, B stored K x N): lane owns 4 columns of C; a wave's
+//    loads of one row of B are 1 KB contiguous; the M values of A a step
+//    needs are the same for every lane (scalar loads).  The workgroup's four
+//    waves take four consecutive K ranges of the chunk and add their partial
+//    columns in wave order through LDS.
+//  * thin_n (N <= 8, A stored M x K): a wave owns 4 rows of C and its lanes
+//    split K, 4 consecutive k per lane per step; the workgroup stages B
+//    (K x N or N x K) through LDS, k-major per column, in pieces of 1024 k.
+//    Lane partial sums are added by a fixed butterfly across the wave.
+// Both take a K chunk per gridDim.y: with one chunk they write C
+// (alpha * sum, then fmaf(beta, C, .) when beta != 0, as every other path);
+// with several they write dense partial slabs that splitk_reduce adds in
+// chunk order.  Every order is fixed, so a call is bit-reproducible.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace sgemm {
+
+namespace {
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kThinThreads = 256;  // four waves
+constexpr int kThinMUnroll = 8;    // rows of B in flight per lane (16 B each)
+constexpr int kThinNRows = 4;      // rows of A (and C) per wave in thin_n
+constexpr int kThinNPiece = 1024;  // k per LDS piece of B in thin_n
+
+// Store one row segment of C from a lane: alpha * v (+ beta * C).
+__device__ __forceinline__ void store_c(float* c, const float* v, int n, float alpha, float beta) {
+    for (int e = 0; e < n; e++) {
+        float r = alpha * v[e];
+        if (beta != 0.0f) r = fmaf(beta, c[e], r);
+        c[e] = r;
+    }
+}
+}  // namespace
+
+// out: C (ldo = ldc) when slab == 0, else the workspace, chunk z at
+// out + z * slab with ldo = N.  N % 4 == 0, B's rows 16-byte aligned.
+template <int MR, bool TA>
+__global__ void __launch_bounds__(kThinThreads)
+thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
+       const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
+       float alpha, float beta) {
+    __shared__ v4f red[3][64][MR];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n0 = (blockIdx.x * 64 + lane) * 4;
+    const int z = blockIdx.y;
+    const int kc0 = z * kchunk, kc1 = min(K, kc0 + kchunk);
+    // Wave w takes the w-th quarter of the chunk.
+    const int q = (kc1 - kc0 + 3) / 4;
+    const int k0 = min(kc1, kc0 + w * q), k1 = min(kc1, k0 + q);
+    v4f acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; m++) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (n0 < N) {
+        const float* bp = B + (int64_t)k0 * ldb + n0;
+        int k = k0;
+        for (; k + kThinMUnroll <= k1; k += kThinMUnroll) {
+            v4f b[kThinMUnroll];
+#pragma unroll
+            for (int u = 0; u < kThinMUnroll; u++)
+                b[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(bp + (int64_t)u * ldb));
+#pragma unroll
+            for (int u = 0; u < kThinMUnroll; u++)
+#pragma unroll
+                for (int m = 0; m < MR; m++) {
+                    const float a = TA ? A[(int64_t)(k + u) * lda + m] : A[(int64_t)m * lda + k + u];
+                    acc[m] += a * b[u];
+                }
+            bp += (int64_t)kThinMUnroll * ldb;
+        }
+        for (; k < k1; k++, bp += ldb) {
+            const v4f b = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(bp));
+#pragma unroll
+            for (int m = 0; m < MR; m++) {
+                const float a = TA ? A[(int64_t)k * lda + m] : A[(int64_t)m * lda + k];
+                acc[m] += a * b;
+            }
+        }
+    }
+    // Waves 1..3 hand their partial columns to wave 0, which adds them in
+    // wave (= k) order.
+    if (w > 0) {
+#pragma unroll
+        for (int m = 0; m < MR; m++) red[w - 1][lane][m] = acc[m];
+    }
+    __syncthreads();
+    if (w > 0 || n0 >= N) return;
+#pragma unroll
+    for (int v = 0; v < 3; v++)
+#pragma unroll
+        for (int m = 0; m < MR; m++) acc[m] += red[v][lane][m];
+    if (slab) {
+        float* o = out + (int64_t)z * slab + n0;
+#pragma unroll
+        for (int m = 0; m < MR; m++) *reinterpret_cast<v4f*>(o + (int64_t)m * ldo) = acc[m];
+    } else {
+#pragma unroll
+        for (int m = 0; m < MR; m++) {
+            const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+            store_c(out + (int64_t)m * ldo + n0, v, 4, alpha, beta);
+        }
+    }
+}
+
+// out as in thin_m (ldo = ldc, or N for the workspace).  K % 4 == 0, A's
+// rows 16-byte aligned.  B element (k, n) is B[k * ldb + n], or
+// B[n * ldb + k] when TB.
+template <int NR, bool TB>
+__global__ void __launch_bounds__(kThinThreads)
+thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
+       const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
+       float alpha, float beta) {
+    // B piece, k-major per column; the pad keeps the 16-byte reads of one
+    // column's k run conflict-free across columns.
+    __shared__ __attribute__((aligned(16))) float bs[NR][kThinNPiece + 4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * 4 + w) * kThinNRows;
+    const int z = blockIdx.y;
+    const int k0 = z * kchunk, k1 = min(K, k0 + kchunk);
+    float acc[kThinNRows][NR];
+#pragma unroll
+    for (int r = 0; r < kThinNRows; r++)
+#pragma unroll
+        for (int n = 0; n < NR; n++) acc[r][n] = 0.0f;
+    const float* ap[kThinNRows];
+    bool live[kThinNRows];
+#pragma unroll
+    for (int r = 0; r < kThinNRows; r++) {
+        live[r] = row0 + r < M;
+        ap[r] = A + (int64_t)(live[r] ? row0 + r : 0) * lda;
+    }
+    for (int p0 = k0; p0 < k1; p0 += kThinNPiece) {
+        const int pk = min(kThinNPiece, k1 - p0);
+        __syncthreads();  // the previous piece is consumed
+        for (int i = threadIdx.x; i < pk * NR; i += kThinThreads) {
+            const int k = TB ? i % pk : i / NR, n = TB ? i / pk : i % NR;
+            bs[n][k] = TB ? B[(int64_t)n * ldb + p0 + k] : B[(int64_t)(p0 + k) * ldb + n];
+        }
+        __syncthreads();
+        // Lane takes k = p0 + 4 lane + 256 t.  pk is a multiple of 4.
+        for (int kk = 4 * lane; kk < pk; kk += 256) {
+            v4f a[kThinNRows];
+#pragma unroll
+            for (int r = 0; r < kThinNRows; r++)
+                a[r] = live[r] ? __builtin_nontemporal_load(reinterpret_cast<const v4f*>(ap[r] + p0 + kk))
+                               : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int n = 0; n < NR; n++) {
+                const v4f b = *reinterpret_cast<const v4f*>(&bs[n][kk]);
+#pragma unroll
+                for (int r = 0; r < kThinNRows; r++)
+                    acc[r][n] += a[r][0] * b[0] + a[r][1] * b[1] + a[r][2] * b[2] + a[r][3] * b[3];
+            }
+        }
+    }
+    // Butterfly over the wave: afterwards every lane holds the sums.
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+#pragma unroll
+        for (int r = 0; r < kThinNRows; r++)
+#pragma unroll
+            for (int n = 0; n < NR; n++) acc[r][n] += __shfl_xor(acc[r][n], d, 64);
+    // Lane r writes row row0 + r.
+#pragma unroll
+    for (int r = 0; r < kThinNRows; r++) {
+        if (lane != r || !live[r]) continue;
+        if (slab) {
+            float* o = out + (int64_t)z * slab + (int64_t)(row0 + r) * ldo;
+#pragma unroll
+            for (int n = 0; n < NR; n++) o[n] = acc[r][n];
+        } else {
+            store_c(out + (int64_t)(row0 + r) * ldo, acc[r], NR, alpha, beta);
+        }
+    }
+}
+
+namespace {
+template <int MR>
+hipError_t launch_thin_m_r(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(g.N, 256), (unsigned)splits);
+    float* out = splits > 1 ? ws : g.C;
+    const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
+    if (g.trans_a)
+        hipLaunchKernelGGL((thin_m<MR, true>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+    else
+        hipLaunchKernelGGL((thin_m<MR, false>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+    return hipGetLastError();
+}
+
+template <int NR>
+hipError_t launch_thin_n_r(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(g.M, 4 * kThinNRows), (unsigned)splits);
+    float* out = splits > 1 ? ws : g.C;
+    const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
+    if (g.trans_b)
+        hipLaunchKernelGGL((thin_n<NR, true>), grid, dim3(kThinThreads), 0, s, (int)g.M, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+    else
+        hipLaunchKernelGGL((thin_n<NR, false>), grid, dim3(kThinThreads), 0, s, (int)g.M, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStream_t s) {
+    hipError_t e;
+    if (p.kind == ThinPlan::THIN_M) {
+        switch (g.M) {
+            case 1: e = launch_thin_m_r<1>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 2: e = launch_thin_m_r<2>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 3: e = launch_thin_m_r<3>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 4: e = launch_thin_m_r<4>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 5: e = launch_thin_m_r<5>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 6: e = launch_thin_m_r<6>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 7: e = launch_thin_m_r<7>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 8: e = launch_thin_m_r<8>(g, p.splits, (int)p.kchunk, ws, s); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (g.N) {
+            case 1: e = launch_thin_n_r<1>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 2: e = launch_thin_n_r<2>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 3: e = launch_thin_n_r<3>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 4: e = launch_thin_n_r<4>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 5: e = launch_thin_n_r<5>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 6: e = launch_thin_n_r<6>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 7: e = launch_thin_n_r<7>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 8: e = launch_thin_n_r<8>(g, p.splits, (int)p.kchunk, ws, s); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (e != hipSuccess || p.splits <= 1) return e;
+    return launch_splitk_reduce(g, p.splits, ws, s);
+}
+
+}  // namespace sgemm

@@ -261,7 +261,8 @@ def test_plan_config_choices(lib):
     # Tile configuration of shape-chosen calls (measured choices on MI355X).
     cfg = lambda M, N, K, **kw: rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED, **kw)
     big = cfg(4096, 4096, 4096)
-    assert big == {"tile": (128, 256), "k_groups": 1, "packed": False, "splits": 1, "kchunk": 4096}
+    assert big == {"engine": "mfma", "tile": (128, 256), "k_groups": 1, "packed": False, "splits": 1,
+                   "kchunk": 4096}
     assert cfg(8192, 8192, 8192)["tile"] == (128, 256)
     assert cfg(4096, 4096, 4096, transb=True)["tile"] == (128, 128)   # 128 x 256 needs A, B as stored
     assert cfg(6144, 6144, 6144)["tile"] == (128, 128)               # 2.25 rounds of 128 x 256
@@ -281,7 +282,7 @@ def test_plan_config_choices(lib):
     assert ragged["packed"] and ragged["tile"] == (64, 64) and ragged["splits"] == 1
     # A thin unaligned operand of a large product is copied; a large one of a
     # memory-bound product, or the operands of a mid-size product, are not.
-    assert cfg(8192, 1, 8192)["packed"] and cfg(3, 8192, 8191)["packed"]
+    assert cfg(8192, 13, 8192)["packed"] and cfg(13, 8192, 8191)["packed"]
     assert not cfg(1, 8191, 8192)["packed"]
     assert not cfg(1024, 1027, 1024)["packed"] and not cfg(1023, 1023, 1023)["packed"]
 
@@ -296,10 +297,39 @@ def test_plan_config_agrees_with_split_plan(lib):
 def test_plan_config_empty_and_errors(lib):
     for M, N, K in [(0, 5, 5), (5, 0, 5), (5, 5, 0)]:
         c = rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
-        assert c == {"tile": (0, 0), "k_groups": 0, "packed": False, "splits": 0, "kchunk": 0}
+        assert c == {"engine": None, "tile": (0, 0), "k_groups": 0, "packed": False, "splits": 0,
+                     "kchunk": 0}
     with pytest.raises(rs.SgemmError):
         rs.plan_config(-1, 4, 4)
     with pytest.raises(rs.SgemmError):
         rs.plan_config(64, 64, 64, lda=10)
-    assert lib.sgemm_plan_config(0, 0, 64, 64, 64, None, 64, None, 64, None, None, None, None,
+    assert lib.sgemm_plan_config(0, 0, 64, 64, 64, None, 64, None, 64, None, None, None, None, None,
                                  None) == 1
+
+
+def test_plan_config_thin(lib):
+    # M <= 8 or N <= 8 with a large operand that suits 16-byte loads, of
+    # 384 MB or more (16 MB for a single column): the thin kernels on the
+    # vector units.
+    cfg = lambda M, N, K, **kw: rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED, **kw)
+    for M in (1, 4, 8):
+        c = cfg(M, 16384, 16384)
+        assert c["engine"] == "thin" and c["tile"] == (M, 256) and c["k_groups"] == 4
+        assert c["splits"] > 1 and c["kchunk"] >= 256
+        assert cfg(M, 8192, 8192)["engine"] == "mfma"             # 268 MB: measured no faster
+    for N in (2, 3, 8):
+        c = cfg(16384, N, 16384)
+        assert c["engine"] == "thin" and c["tile"] == (16, N) and c["kchunk"] % 1024 == 0
+        assert cfg(8192, N, 8192)["engine"] == "mfma"
+    assert cfg(8192, 1, 8192)["engine"] == "thin"                 # one column: from 16 MB
+    assert cfg(4096, 1, 1024)["engine"] == "thin"
+    assert cfg(4096, 1, 1020)["engine"] == "mfma"
+    assert cfg(16384, 8, 16384, transb=True)["engine"] == "thin"  # B is staged, any orientation
+    assert cfg(8, 16384, 16384, transa=True)["engine"] == "thin"  # A read by scalar loads
+    assert cfg(16384, 8, 16384, transa=True)["engine"] == "mfma"  # the streamed side must be row-major
+    assert cfg(8, 16384, 16384, transb=True)["engine"] == "mfma"
+    assert cfg(16, 16384, 16384)["engine"] == "mfma"              # not thin
+    assert cfg(1, 16383, 16384)["engine"] == "mfma"               # B rows not 16-byte chunks
+    assert cfg(16384, 1, 16383)["engine"] == "mfma"               # A rows not 16-byte chunks
+    # A split request bypasses the thin path.
+    assert rs.split_plan(8, 16384, 16384, A_ptr=ALIGNED, B_ptr=ALIGNED, splits=1) == (1, 16384)

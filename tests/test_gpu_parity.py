@@ -253,9 +253,9 @@ def test_narrow_outputs_auto(shape):
 
 
 # Thin unaligned operands of large products: the packing pre-pass copies the
-# thin one (B with 1 or 3 columns, A with K = 8191) and the product runs on
-# 16-byte loads with a K split, all through one workspace.
-THIN = [(8192, 1, 8192), (8192, 3, 4096), (3, 8192, 8191)]
+# thin one (B with 9 or 13 columns, A with 13 rows and K = 8191) and the
+# product runs on 16-byte loads with a K split, all through one workspace.
+THIN = [(8192, 13, 8192), (8192, 9, 4096), (13, 8192, 8191)]
 
 
 @pytest.mark.parametrize("shape", THIN, ids=lambda s: "x".join(map(str, s)))

@@ -1,0 +1,111 @@
+"""GPU parity of the thin-product kernels (M <= 8 or N <= 8 with a large
+streamed operand), through the C ABI.
+
+Every call goes through the shape-chosen entry point (sgemm_f32_ex) and is
+first checked to take the thin path (sgemm_plan_config); the result must meet
+the general bound against the CPU oracle (|C - C_ref| <= 4 K 2^-24 |alpha|
+sum|ab| + 2 * 2^-24 (|alpha sum ab| + |beta C0|)), and with integer operands
+and small integer alpha, beta it must equal the oracle bit for bit.  Shapes
+cover M and N from 1 to 8, K chunks split and whole, K not a multiple of
+the kernels' pieces, outputs not a multiple of a workgroup's columns or
+rows, and A or B stored transposed where the path allows it."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check
+import roofline_sgemm_f32_amd as rs
+from roofline_sgemm_f32_amd.inputs import as_numpy, make_operands
+from tests.gpu_util import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rs.load()
+    oracle.load()
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_thin(ta, tb, M, N, K, alpha, beta, dist, seed):
+    A, B = make_operands(M, N, K, dist, seed)
+    C0 = make_operands(M, 1, N, dist, seed + 1)[0]
+    As = A.t().contiguous() if ta else A.contiguous()
+    Bs = B.t().contiguous() if tb else B.contiguous()
+    Ad, Bd = to_device(As), to_device(Bs)
+    plan = rs.plan_config(M, N, K, transa=bool(ta), transb=bool(tb), lda=Ad.stride(0),
+                          ldb=Bd.stride(0), A_ptr=Ad.data_ptr(), B_ptr=Bd.data_ptr())
+    note(f"[thin] {ta}{tb} {M}x{N}x{K} alpha={alpha} beta={beta} {dist} plan={plan}")
+    assert plan["engine"] == "thin", plan
+    Cbuf = torch.full((M * N + 16,), 777.0, device="cuda")
+    Cd = torch.as_strided(Cbuf, (M, N), (N, 1))
+    Cd.copy_(C0)
+    st = rs.load().sgemm_f32_ex(int(ta), int(tb), M, N, K, alpha, Ad.data_ptr(), Ad.stride(0),
+                                Bd.data_ptr(), Bd.stride(0), beta, Cbuf.data_ptr(), N,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0, rs.status_string(st)
+    torch.cuda.synchronize()
+    assert torch.all(Cbuf[M * N:].cpu() == 777.0), "wrote past C"
+    got = Cd.cpu().numpy()
+    ref, S, E = oracle.sgemm_ex_f64(ta, tb, alpha, as_numpy(As), as_numpy(Bs), beta,
+                                    None if beta == 0 else as_numpy(C0))
+    return got, ref, S, E, plan
+
+
+# (transa, transb, M, N, K).  The streamed operand is 384 MB or more (16 MB
+# or more for a single column), where the plan takes the thin path.
+THIN_M = [(0, 0, 1, 24576, 4096), (1, 0, 3, 16388, 6147), (0, 0, 8, 8196, 12288)]
+THIN_N = [(0, 0, 4096, 1, 1024), (0, 0, 4100, 1, 1028), (0, 1, 16385, 2, 6144), (0, 0, 12289, 5, 8196),
+          (0, 1, 8193, 8, 12288)]
+
+
+@pytest.mark.parametrize("case", THIN_M + THIN_N, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+def test_thin_uniform(case):
+    ta, tb, M, N, K = case
+    for alpha, beta in [(1.0, 0.0), (-1.5, 0.75)]:
+        got, ref, S, E, _ = run_thin(ta, tb, M, N, K, alpha, beta, "uniform", seed=M + N + K)
+        rep = check.check_ex(got, ref, S, E, K)
+        assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("case", THIN_M + THIN_N, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+def test_thin_integer_exact(case):
+    ta, tb, M, N, K = case
+    for alpha, beta in [(1.0, 0.0), (2.0, -1.0)]:
+        got, ref, _, _, _ = run_thin(ta, tb, M, N, K, alpha, beta, "int", seed=3 * M + K)
+        assert np.array_equal(got.astype(np.float64), ref), (case, alpha, beta)
+
+
+def test_thin_split_and_whole_chunks():
+    # The same thin shapes with K split across workgroups and unsplit.
+    splits = {}
+    for case in [(0, 0, 8, 16384, 8192), (0, 0, 8192, 1, 8192), (0, 0, 100000, 4, 1024)]:
+        _, _, M, N, K = case
+        got, ref, S, E, plan = run_thin(*case, 1.0, 0.0, "uniform", seed=11)
+        splits[(M, N, K)] = plan["splits"]
+        assert check.check_ex(got, ref, S, E, K)["ok"]
+    assert splits[(8, 16384, 8192)] > 1 and splits[(8192, 1, 8192)] > 1
+    assert splits[(100000, 4, 1024)] == 1
+
+
+def test_thin_repeated_calls_identical():
+    A, B = make_operands(4, 16384, 8192, "uniform", 12)
+    Ad, Bd = A.cuda(), B.cuda()
+    assert rs.plan_config(4, 16384, 8192, A_ptr=Ad.data_ptr(), B_ptr=Bd.data_ptr())["engine"] == "thin"
+    outs = []
+    for _ in range(3):
+        C = torch.empty((4, 16384), device="cuda")
+        rs.sgemm(Ad, Bd, out=C)
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
