@@ -68,3 +68,39 @@ def test_capture_and_replay(shape, what):
     ref, S = oracle.sgemm_f64(as_numpy(A), as_numpy(B))
     assert check.check(out.cpu().numpy(), ref, S, K)["ok"]
     assert check.check(other.cpu().numpy(), ref, S, K)["ok"]
+
+
+@pytest.mark.parametrize("shape", [(4096, 1, 1024), (8192, 1, 8192)], ids=lambda s: "x".join(map(str, s)))
+def test_capture_thin(shape):
+    # Thin products: a captured call runs the thin kernel with one K chunk.
+    # (4096, 1, 1024) takes one chunk eagerly too, so replays equal the eager
+    # call; (8192, 1, 8192) splits K eagerly, so replays are checked against
+    # each other and the oracle.
+    M, N, K = shape
+    lib = rs.load()
+    A, B = make_operands(M, N, K, "uniform", seed=M + K)
+    Ad, Bd = A.cuda(), B.cuda()
+    plan = rs.plan_config(M, N, K, A_ptr=Ad.data_ptr(), B_ptr=Bd.data_ptr())
+    assert plan["engine"] == "thin"
+    eager = torch.empty((M, N), device="cuda")
+    call(lib, Ad, Bd, eager, 0, torch.cuda.current_stream().cuda_stream)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        call(lib, Ad, Bd, out, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    first = None
+    for r in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.clone()
+        assert torch.equal(out, first), f"replay {r} differs from the first"
+    if plan["splits"] == 1:
+        assert torch.equal(first, eager)
+    ref, S = oracle.sgemm_f64(as_numpy(A), as_numpy(B))
+    assert check.check(first.cpu().numpy(), ref, S, K)["ok"]
+    assert check.check(eager.cpu().numpy(), ref, S, K)["ok"]
