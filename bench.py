@@ -334,7 +334,8 @@ def ladder(args, out):
 
 
 # Small-shape path: shapes whose 64 x 64 tiles underfill the 256 compute
-# units (the two small workloads plus K-heavy outputs), timed with the K
+# units (the two small workloads plus K-heavy and skinny outputs), and one
+# thin product (a single row of C, 1 GiB of B streamed), timed with the K
 # split the library chooses and unsplit.
 SMALL_SHAPES = {
     "square256": None,
@@ -344,6 +345,7 @@ SMALL_SHAPES = {
     "kheavy256x256x16384": (256, 256, 16384),
     "kheavy1024x1024x4096": (1024, 1024, 4096),
     "skinny64x8192x8192": (64, 8192, 8192),
+    "thin1x16384x16384": (1, 16384, 16384),
 }
 
 
@@ -375,6 +377,8 @@ def small_shapes(reps: int, only=None):
                 C.data_ptr(), C.stride(0))
         chunks, kchunk = rs.split_plan(M, N, K, lda=A.stride(0), ldb=B.stride(0),
                                        A_ptr=A.data_ptr(), B_ptr=B.data_ptr())
+        plan = rs.plan_config(M, N, K, lda=A.stride(0), ldb=B.stride(0), A_ptr=A.data_ptr(),
+                              B_ptr=B.data_ptr())
 
         def call(splits):
             def fn():
@@ -403,13 +407,13 @@ def small_shapes(reps: int, only=None):
             rows.append({"shape": name, "M": M, "N": N, "K": K, "gate": False})
             del A, B, C
             continue
-        rec = {"shape": name, "gate": True, "M": M, "N": N, "K": K, "chunks": chunks, "kchunk": kchunk,
+        rec = {"shape": name, "gate": True, "engine": plan["engine"], "tile": list(plan["tile"]), "M": M, "N": N, "K": K, "chunks": chunks, "kchunk": kchunk,
                "us_per_call": round(1e3 * t_auto, 2), "gflops": round(m.gflops(flops, t_auto), 1),
                "unsplit_us_per_call": round(1e3 * t_one, 2),
                "unsplit_gflops": round(m.gflops(flops, t_one), 1),
                "speedup_vs_unsplit": round(t_one / t_auto, 3)}
         rows.append(rec)
-        log(f"  small {name:22s} chunks={chunks:2d} {rec['us_per_call']:9.2f} us "
+        log(f"  small {name:22s} {plan['engine']:4s} chunks={chunks:2d} {rec['us_per_call']:9.2f} us "
             f"{rec['gflops']:9.1f} GFLOP/s (unsplit {rec['unsplit_us_per_call']:9.2f} us) "
             f"x{rec['speedup_vs_unsplit']}")
         del A, B, C

@@ -157,10 +157,12 @@ def small_shape_points(bench_line: dict) -> list[Point]:
         flop = m.sgemm_flops(M, N, K)
         rd = 4.0 * (M * K + K * N) / 1e6
         wr = 4.0 * M * N / 1e6
-        pts.append(Point(f"{r['shape']} ({r['chunks']} chunk{'s' if r['chunks'] > 1 else ''})",
+        kind = "thin kernel, " if r.get("engine") == "thin" else ""
+        pts.append(Point(f"{r['shape']} ({kind}{r['chunks']} chunk{'s' if r['chunks'] > 1 else ''})",
                          r["us_per_call"] / 1e3, flop, rd, wr))
-        if r["chunks"] > 1:
-            pts.append(Point(f"{r['shape']} unsplit", r["unsplit_us_per_call"] / 1e3, flop, rd, wr))
+        if r["chunks"] > 1 or kind:
+            other = "matrix cores, unsplit" if kind else "unsplit"
+            pts.append(Point(f"{r['shape']} {other}", r["unsplit_us_per_call"] / 1e3, flop, rd, wr))
     return pts
 
 

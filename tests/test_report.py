@@ -55,9 +55,12 @@ def test_small_shape_points():
          "unsplit_us_per_call": 5.0},
         {"shape": "kheavy", "M": 128, "N": 128, "K": 4096, "chunks": 16, "us_per_call": 13.0,
          "unsplit_us_per_call": 30.0},
-        {"shape": "failed", "M": 64, "N": 64, "K": 64, "gate": False}]}
+        {"shape": "failed", "M": 64, "N": 64, "K": 64, "gate": False},
+        {"shape": "thin", "M": 1, "N": 4096, "K": 4096, "chunks": 4, "engine": "thin",
+         "us_per_call": 20.0, "unsplit_us_per_call": 30.0}]}
     pts = report.small_shape_points(line)
-    assert [p.kernel for p in pts] == ["square256 (1 chunk)", "kheavy (16 chunks)", "kheavy unsplit"]
+    assert [p.kernel for p in pts] == ["square256 (1 chunk)", "kheavy (16 chunks)", "kheavy unsplit",
+                                       "thin (thin kernel, 4 chunks)", "thin matrix cores, unsplit"]
     # 2 * 256^3 FLOP in 5 us; algorithmic bytes 4 * 3 * 256^2.
     assert pts[0].tflops == pytest.approx(2 * 256 ** 3 / 5e-6 / 1e12)
     assert pts[0].intensity == pytest.approx(2 * 256 ** 3 / (12 * 256 ** 2))
