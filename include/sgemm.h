@@ -55,7 +55,9 @@ typedef enum sgemm_variant {
     SGEMM_K2_LDS_TILED = 2,       /* 32 x 32 LDS tiles of A and B per K step; one output per lane */
     SGEMM_K3_REGTILE_DB = 3,      /* 128 x 128 workgroup tile, 8 x 8 outputs per lane in VGPRs, LDS double buffer */
     SGEMM_K4_MFMA = 4,            /* FP32 matrix-core kernel (v_mfma_f32_32x32x2_f32), direct global->LDS
-                                     loads; 128 x 128 or 64 x 64 workgroup tiles chosen by shape */
+                                     loads; 128 x 256, 128 x 128, 64 x 64 or 32 x 32 workgroup tiles, K
+                                     split and operand packing chosen by shape (sgemm_plan_config); thin
+                                     products (M or N <= 8, large operand) run on the vector units */
     SGEMM_K2_LDS_TILED16 = 5,     /* as K2 with 16 x 16 tiles */
     SGEMM_K2_LDS_TILED_PAD1 = 6,  /* as K2 with rows padded by one float (LDS bank comparison) */
     SGEMM_K0_NAIVE = 7,           /* one output per lane, lanes down a column of C (uncoalesced foil) */
