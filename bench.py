@@ -203,6 +203,9 @@ def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float, threads: int | None = 
             base["cpu"] = model
     except OSError:
         pass
+    # The oracle runs `cores` POSIX threads whatever OpenMP is set to; the
+    # environment's OpenMP setting is recorded for context.
+    base["omp_num_threads_env"] = os.environ.get("OMP_NUM_THREADS")
     gate = {"rows_checked": len(rows), "ok": rep["ok"], "max_bound_util": rep["max_bound_util"],
             "max_rel_err_page": rep["max_rel_err_page"], "n_violations": rep["n_violations"]}
     return base, gate
