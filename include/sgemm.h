@@ -126,8 +126,12 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
  * stream-ordered (from a memory pool the library creates) on first need,
  * grown on demand up to 256 MiB and kept for later calls; a larger request
  * gets a buffer of its own, freed stream-ordered after the call.  Split calls
- * on one device take the buffer in turn (a host lock around their launches;
- * a call on another stream than the previous one waits for it on the GPU).
+ * on one device take the buffer in turn (a host lock around their launches).
+ * While every call has used one stream, the stream alone orders them; the
+ * first call on a second stream synchronizes the device once (as
+ * hipDeviceSynchronize, so it must not coincide with a graph capture on
+ * another thread), and from then on a call on another stream than the
+ * previous one waits for it on the GPU through an event.
  * If the workspace cannot be allocated the product runs unsplit, and so do
  * calls made while `stream` is being captured into a graph (the workspace
  * paths, split-K and the packing of unaligned operands, are skipped there,

@@ -211,14 +211,20 @@ static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
     if (!k4_supports(gp)) return false;
     // Worth a copy launch: outputs of at least 512 tiles of 64 x 64; or a
     // product moving 64 MB or more whose copies are at most 1/8 of that, as
-    // when a narrow or thin operand is the only unaligned one (8192 x 1 x
-    // 8192: 79 -> 60 us; 3 x 8192 x 8191: 79 -> 59).  Copying a large
-    // operand of a mid-size product did not pay (1024 x 1027 x 1024: 41.7
-    // -> 45.3 us; 1 x 8191 x 8192, B copied: 79 -> 144).
+    // when a narrow or thin operand is the only unaligned one (8192 x 13 x
+    // 8192: 82 -> 61 us; 13 x 8192 x 8191); or 4 GFLOP or more with copies
+    // of at most 64 MB and 1 byte per 100 FLOP (767 x 769 x 4095: 91 -> 72
+    // us; 1025 x 1025 x 2047: 78 -> 70).  A copy of 8 to 17 MB takes about
+    // 9 us, so it did not pay below that (1023^3: 32.8 -> 33.2 us; 1024 x
+    // 1027 x 1024: 41.6 -> 42.7), nor where a large operand of a memory-bound
+    // product is copied (1 x 8191 x 8192: 79 -> 144).
     const double moved = 4.0 * (double(g.M) * g.K + double(g.K) * g.N + double(g.M) * g.N);
+    const double flop = 2.0 * double(g.M) * double(g.N) * double(g.K);
     const double copied = double(pk->a_bytes + pk->b_bytes);
-    if (ceil_div(g.M, 64) * ceil_div(g.N, 64) < 512 && !(moved >= 64e6 && copied <= moved / 8))
-        return false;
+    const bool big_output = ceil_div(g.M, 64) * ceil_div(g.N, 64) >= 512;
+    const bool thin_copy = moved >= 64e6 && copied <= moved / 8;
+    const bool heavy = flop >= 4e9 && copied <= 64e6 && copied <= flop / 100;
+    if (!big_output && !thin_copy && !heavy) return false;
     pk->p = k4_plan(gp, 0);
     pk->gp = gp;
     return true;

@@ -14,28 +14,24 @@
 namespace sgemm {
 
 namespace {
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 struct PackJob {
     const float* src;
     int64_t rows, cols, ld;
     float* dst;
 };
 
-// gridDim.y jobs (one or two matrices), each copied by a grid-stride loop
-// over its 4-float output chunks.
+// gridDim.y jobs (one or two matrices).  A workgroup copies whole rows, a
+// grid-stride loop over them; lane i moves elements i, i + 256, ... of a
+// row, so every load and store instruction covers 256 consecutive bytes
+// whatever the source's alignment.  No division per element.
 __global__ void __launch_bounds__(256)
 pack_rows(PackJob j0, PackJob j1) {
     const PackJob j = blockIdx.y == 0 ? j0 : j1;
-    const int64_t ld_dst = (j.cols + 3) / 4 * 4, q = ld_dst / 4, total = j.rows * q;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / q, c = (i % q) * 4;
+    const int64_t ld_dst = (j.cols + 3) / 4 * 4;
+    for (int64_t r = blockIdx.x; r < j.rows; r += gridDim.x) {
         const float* s = j.src + r * j.ld;
-        v4f v;
-#pragma unroll
-        for (int e = 0; e < 4; e++) v[e] = c + e < j.cols ? s[c + e] : 0.0f;
-        *(v4f*)(j.dst + r * ld_dst + c) = v;
+        float* d = j.dst + r * ld_dst;
+        for (int64_t c = threadIdx.x; c < ld_dst; c += blockDim.x) d[c] = c < j.cols ? s[c] : 0.0f;
     }
 }
 }  // namespace
@@ -46,10 +42,10 @@ hipError_t launch_pack(const float* src, int64_t rows, int64_t cols, int64_t ld,
                        const float* src2, int64_t rows2, int64_t cols2, int64_t ld2, float* dst2,
                        hipStream_t s) {
     const PackJob j0{src, rows, cols, ld, dst}, j1{src2, rows2, cols2, ld2, dst2};
-    int64_t chunks = rows * (packed_ld(cols) / 4);
-    if (src2) chunks = std::max(chunks, rows2 * (packed_ld(cols2) / 4));
-    hipLaunchKernelGGL(pack_rows, dim3(grid_for(ceil_div(chunks, 256)), src2 ? 2 : 1), dim3(256), 0, s,
-                       j0, j1);
+    // Up to 1024 workgroups per matrix (4 per CU), whole rows each.
+    const int64_t rmax = src2 ? std::max(rows, rows2) : rows;
+    const unsigned grid = unsigned(std::max<int64_t>(1, std::min<int64_t>(rmax, 1024)));
+    hipLaunchKernelGGL(pack_rows, dim3(grid, src2 ? 2 : 1), dim3(256), 0, s, j0, j1);
     return hipGetLastError();
 }
 

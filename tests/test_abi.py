@@ -285,6 +285,9 @@ def test_plan_config_choices(lib):
     assert cfg(8192, 13, 8192)["packed"] and cfg(13, 8192, 8191)["packed"]
     assert not cfg(1, 8191, 8192)["packed"]
     assert not cfg(1024, 1027, 1024)["packed"] and not cfg(1023, 1023, 1023)["packed"]
+    # 4 GFLOP or more with small copies: copied (and split on the copies).
+    assert cfg(767, 769, 4095)["packed"] and cfg(513, 511, 8193)["packed"]
+    assert not cfg(64, 64, 1000001)["packed"]      # copies of 512 MB for an 8 GFLOP product
 
 
 def test_plan_config_agrees_with_split_plan(lib):

@@ -205,6 +205,22 @@ def test_ex_packed_operands(ta, tb, shape):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("shape", [(767, 769, 4095), (513, 511, 8193), (1025, 1025, 2047)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ex_heavy_mid_size_packed(shape):
+    # Mid-size outputs with a long K and unaligned operands: 4 GFLOP or more,
+    # so the plan copies both operands and splits K on the copies.
+    M, N, K = shape
+    plan = rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)
+    print(f"[heavy packed] {M}x{N}x{K} plan {plan}", flush=True)
+    assert plan["packed"] and plan["splits"] > 1
+    got, ref, _, _ = run_ex(0, 0, M, N, K, 2.0, -1.0, "int", seed=M + 3)
+    assert np.array_equal(got.astype(np.float64), ref)
+    got, ref, S, E = run_ex(0, 0, M, N, K, 1.0, 0.5, "uniform", seed=M + 4)
+    rep = check.check_ex(got, ref, S, E, K)
+    assert rep["ok"], rep
+
+
 def test_ex_packed_and_split():
     # Unaligned operands whose packed copies get a split plan (600 tiles of
     # 64 x 64, under 4 per CU, K = 4095): packing and split share one
