@@ -265,28 +265,34 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
 
 // Thin products (one side of C at most 8) stream their large operand on the
 // vector units (thin.hip) when it suits 16-byte loads (B stored K x N for
-// M <= 8, A stored M x K for N <= 8) and is 384 MB or more, or, for a single
-// column of C, 16 MB or more.  Measured against the matrix-core path, whose
-// 32 x 32 tiles stream the operand too (MI355X, back-to-back calls, us):
-// 1 x 16384 x 16384 290 -> 168, 16384 x 8 x 16384 296 -> 223, 2 x 65536 x
-// 4096 286 -> 174, 100000 x 4 x 1024 127 -> 80, 8192 x 1 x 8192 79 -> 68;
-// at 268 MB with more than one column the thin kernels were no faster (1 x
-// 8192 x 8192 55 -> 67, 8192 x 8 x 8192 56 -> 82): the fixed costs of the
-// split and of staging B weigh more there.  K is split so that about 1024
-// workgroups of 4 waves (4 per CU) keep loads in flight; a chunk keeps at
-// least 256 of K (thin_m) or one 1024-k piece (thin_n).
+// M <= 8, A stored M x K for N <= 8) and is large enough: 384 MB or more;
+// for N <= 4, 256 MB; for a single column, 16 MB.  Measured against the
+// matrix-core path, whose 32 x 32 tiles stream the operand too (MI355X,
+// back-to-back launches, us): 1 x 16384 x 16384 290 -> 168, 16384 x 8 x
+// 16384 296 -> 187, 2 x 65536 x 4096 286 -> 174, 100000 x 4 x 1024 127 ->
+// 80, 8192 x 4 x 8192 56 -> 51, 8192 x 1 x 8192 79 -> 48; at 268 MB the
+// thin kernels were no faster for M <= 8 or 5 <= N <= 8 (1 x 8192 x 8192
+// 55 -> 55, 8192 x 8 x 8192 56 -> 62): the fixed costs of the split and of
+// staging B weigh more there.  thin_n runs workgroups of 8 waves that keep
+// two steps' loads in flight, except for one or two columns of C with
+// M >= 16384, where 4 waves of one step each were faster (100000 x 1 x
+// 4096 300 -> 274, 65536 x 2 x 4096 204 -> 181, 16384 x 1 x 16384 168 ->
+// 162).  K is split so that about 1024 workgroups keep loads in flight; a
+// chunk keeps at least 256 of K (thin_m) or one 1024-k piece (thin_n).
 ThinPlan thin_plan(const GemmArgs& g) {
     ThinPlan t;
-    constexpr int64_t kTarget = 1024, kMinBytes = int64_t(384) << 20, kMinColumn = int64_t(16) << 20;
+    constexpr int64_t kTarget = 1024, kMinBytes = int64_t(384) << 20;
+    constexpr int64_t kMinFewColumns = int64_t(256) << 20, kMinColumn = int64_t(16) << 20;
     int64_t groups = 0, min_chunk = 0, quantum = 4;
+    const int64_t min_n = g.N == 1 ? kMinColumn : g.N <= 4 ? kMinFewColumns : kMinBytes;
     if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes && rows_vec(g.B, g.ldb, g.N)) {
         t.kind = ThinPlan::THIN_M;
         groups = ceil_div(g.N, 256);
         min_chunk = 256;
-    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= (g.N == 1 ? kMinColumn : kMinBytes) &&
-               rows_vec(g.A, g.lda, g.K)) {
+    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= min_n && rows_vec(g.A, g.lda, g.K)) {
         t.kind = ThinPlan::THIN_N;
-        groups = ceil_div(g.M, 16);
+        t.waves = g.N <= 2 && g.M >= 16384 ? 4 : 8;
+        groups = ceil_div(g.M, 4 * t.waves);
         min_chunk = 1024;
         quantum = 1024;
     } else {
@@ -307,7 +313,7 @@ PlanInfo plan_info(const GemmArgs& g, int requested) {
         const ThinPlan t = thin_plan(g);
         if (t.kind != ThinPlan::NONE) {
             info.engine = 2;
-            info.tile_m = t.kind == ThinPlan::THIN_M ? (int)g.M : 16;
+            info.tile_m = t.kind == ThinPlan::THIN_M ? (int)g.M : 4 * t.waves;
             info.tile_n = t.kind == ThinPlan::THIN_M ? 256 : (int)g.N;
             info.k_groups = t.kind == ThinPlan::THIN_M ? 4 : 1;
             info.splits = t.splits;

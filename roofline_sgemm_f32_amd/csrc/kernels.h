@@ -57,10 +57,11 @@ struct SplitPlan {
 SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
 // Thin products on the vector units (thin.hip): M <= 8 (B streamed) or
 // N <= 8 (A streamed), in `splits` K chunks of kchunk whose partial
-// products take ws_floats floats of workspace.
+// products take ws_floats floats of workspace; thin_n workgroups of `waves`
+// waves (8, or 4 for N <= 2), 4 rows of C each.
 struct ThinPlan {
     enum Kind { NONE, THIN_M, THIN_N } kind = NONE;
-    int splits = 1;
+    int splits = 1, waves = 8;
     int64_t kchunk = 0, ws_floats = 0;
 };
 // Whether a shape-chosen call takes the thin path, and how.

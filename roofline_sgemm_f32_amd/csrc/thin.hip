@@ -14,9 +14,11 @@
 //    waves take four consecutive K ranges of the chunk and add their partial
 //    columns in wave order through LDS.
 //  * thin_n (N <= 8, A stored M x K): a wave owns 4 rows of C and its lanes
-//    split K, 4 consecutive k per lane per step; the workgroup stages B
-//    (K x N or N x K) through LDS, k-major per column, in pieces of 1024 k.
-//    Lane partial sums are added by a fixed butterfly across the wave.
+//    split K, 4 consecutive k per lane per step, UN steps' loads in flight;
+//    the workgroup (WAVES waves: 8 with UN 2, or 4 with UN 1 for long A of
+//    one or two columns) stages B (K x N or N x K) through LDS, k-major per
+//    column, in pieces of 1024 k.  Lane partial sums are added by a fixed
+//    butterfly across the wave.
 // Both take a K chunk per gridDim.y: with one chunk they write C
 // (alpha * sum, then fmaf(beta, C, .) when beta != 0, as every other path);
 // with several they write dense partial slabs that splitk_reduce adds in
@@ -30,10 +32,10 @@ namespace sgemm {
 namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kThinThreads = 256;  // four waves
-constexpr int kThinMUnroll = 8;    // rows of B in flight per lane (16 B each)
-constexpr int kThinNRows = 4;      // rows of A (and C) per wave in thin_n
-constexpr int kThinNPiece = 1024;  // k per LDS piece of B in thin_n
+constexpr int kThinThreads = 256;   // thin_m: four waves
+constexpr int kThinMUnroll = 8;     // rows of B in flight per lane (16 B each)
+constexpr int kThinNRows = 4;       // rows of A (and C) per wave in thin_n
+constexpr int kThinNPiece = 1024;   // k per LDS piece of B in thin_n
 
 // Store one row segment of C from a lane: alpha * v (+ beta * C).
 __device__ __forceinline__ void store_c(float* c, const float* v, int n, float alpha, float beta) {
@@ -117,8 +119,8 @@ thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
 // out as in thin_m (ldo = ldc, or N for the workspace).  K % 4 == 0, A's
 // rows 16-byte aligned.  B element (k, n) is B[k * ldb + n], or
 // B[n * ldb + k] when TB.
-template <int NR, bool TB>
-__global__ void __launch_bounds__(kThinThreads)
+template <int NR, bool TB, int WAVES, int UN>
+__global__ void __launch_bounds__(64 * WAVES)
 thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
        const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
        float alpha, float beta) {
@@ -126,7 +128,7 @@ thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
     // column's k run conflict-free across columns.
     __shared__ __attribute__((aligned(16))) float bs[NR][kThinNPiece + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int row0 = (blockIdx.x * 4 + w) * kThinNRows;
+    const int row0 = (blockIdx.x * WAVES + w) * kThinNRows;
     const int z = blockIdx.y;
     const int k0 = z * kchunk, k1 = min(K, k0 + kchunk);
     float acc[kThinNRows][NR];
@@ -144,24 +146,35 @@ thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
     for (int p0 = k0; p0 < k1; p0 += kThinNPiece) {
         const int pk = min(kThinNPiece, k1 - p0);
         __syncthreads();  // the previous piece is consumed
-        for (int i = threadIdx.x; i < pk * NR; i += kThinThreads) {
+        for (int i = threadIdx.x; i < pk * NR; i += 64 * WAVES) {
             const int k = TB ? i % pk : i / NR, n = TB ? i / pk : i % NR;
             bs[n][k] = TB ? B[(int64_t)n * ldb + p0 + k] : B[(int64_t)(p0 + k) * ldb + n];
         }
         __syncthreads();
-        // Lane takes k = p0 + 4 lane + 256 t.  pk is a multiple of 4.
-        for (int kk = 4 * lane; kk < pk; kk += 256) {
-            v4f a[kThinNRows];
+        // Lane takes k = p0 + 4 lane + 256 t, UN steps t per batch with all
+        // their loads issued first.  pk is a multiple of 4.
+        for (int kb = 0; kb < pk; kb += 256 * UN) {
+            v4f a[UN][kThinNRows];
 #pragma unroll
-            for (int r = 0; r < kThinNRows; r++)
-                a[r] = live[r] ? __builtin_nontemporal_load(reinterpret_cast<const v4f*>(ap[r] + p0 + kk))
-                               : v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int n = 0; n < NR; n++) {
-                const v4f b = *reinterpret_cast<const v4f*>(&bs[n][kk]);
+            for (int u = 0; u < UN; u++) {
+                const int kk = kb + 256 * u + 4 * lane;
 #pragma unroll
                 for (int r = 0; r < kThinNRows; r++)
-                    acc[r][n] += a[r][0] * b[0] + a[r][1] * b[1] + a[r][2] * b[2] + a[r][3] * b[3];
+                    a[u][r] = live[r] && kk < pk
+                                  ? __builtin_nontemporal_load(reinterpret_cast<const v4f*>(ap[r] + p0 + kk))
+                                  : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int u = 0; u < UN; u++) {
+                const int kk = kb + 256 * u + 4 * lane;
+                if (kk >= pk) continue;
+#pragma unroll
+                for (int n = 0; n < NR; n++) {
+                    const v4f b = *reinterpret_cast<const v4f*>(&bs[n][kk]);
+#pragma unroll
+                    for (int r = 0; r < kThinNRows; r++)
+                        acc[r][n] += a[u][r][0] * b[0] + a[u][r][1] * b[1] + a[u][r][2] * b[2] + a[u][r][3] * b[3];
+                }
             }
         }
     }
@@ -201,17 +214,29 @@ hipError_t launch_thin_m_r(const GemmArgs& g, int splits, int kchunk, float* ws,
     return hipGetLastError();
 }
 
-template <int NR>
-hipError_t launch_thin_n_r(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
-    const dim3 grid((unsigned)ceil_div(g.M, 4 * kThinNRows), (unsigned)splits);
+template <int NR, int WAVES, int UN>
+void launch_thin_n_w(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(g.M, WAVES * kThinNRows), (unsigned)splits);
     float* out = splits > 1 ? ws : g.C;
     const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
     if (g.trans_b)
-        hipLaunchKernelGGL((thin_n<NR, true>), grid, dim3(kThinThreads), 0, s, (int)g.M, (int)g.K,
+        hipLaunchKernelGGL((thin_n<NR, true, WAVES, UN>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
                            kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
     else
-        hipLaunchKernelGGL((thin_n<NR, false>), grid, dim3(kThinThreads), 0, s, (int)g.M, (int)g.K,
+        hipLaunchKernelGGL((thin_n<NR, false, WAVES, UN>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
                            kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+}
+
+template <int NR>
+hipError_t launch_thin_n_r(const GemmArgs& g, const ThinPlan& p, float* ws, hipStream_t s) {
+    if constexpr (NR <= 2) {
+        if (p.waves == 4) {
+            launch_thin_n_w<NR, 4, 1>(g, p.splits, (int)p.kchunk, ws, s);
+            return hipGetLastError();
+        }
+    }
+    if (p.waves != 8) return hipErrorInvalidValue;
+    launch_thin_n_w<NR, 8, 2>(g, p.splits, (int)p.kchunk, ws, s);
     return hipGetLastError();
 }
 }  // namespace
@@ -232,14 +257,14 @@ hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStrea
         }
     } else {
         switch (g.N) {
-            case 1: e = launch_thin_n_r<1>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 2: e = launch_thin_n_r<2>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 3: e = launch_thin_n_r<3>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 4: e = launch_thin_n_r<4>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 5: e = launch_thin_n_r<5>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 6: e = launch_thin_n_r<6>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 7: e = launch_thin_n_r<7>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 8: e = launch_thin_n_r<8>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 1: e = launch_thin_n_r<1>(g, p, ws, s); break;
+            case 2: e = launch_thin_n_r<2>(g, p, ws, s); break;
+            case 3: e = launch_thin_n_r<3>(g, p, ws, s); break;
+            case 4: e = launch_thin_n_r<4>(g, p, ws, s); break;
+            case 5: e = launch_thin_n_r<5>(g, p, ws, s); break;
+            case 6: e = launch_thin_n_r<6>(g, p, ws, s); break;
+            case 7: e = launch_thin_n_r<7>(g, p, ws, s); break;
+            case 8: e = launch_thin_n_r<8>(g, p, ws, s); break;
             default: return hipErrorInvalidValue;
         }
     }

@@ -312,8 +312,8 @@ def test_plan_config_empty_and_errors(lib):
 
 def test_plan_config_thin(lib):
     # M <= 8 or N <= 8 with a large operand that suits 16-byte loads, of
-    # 384 MB or more (16 MB for a single column): the thin kernels on the
-    # vector units.
+    # 384 MB or more (256 MB for 2 to 4 columns, 16 MB for a single column):
+    # the thin kernels on the vector units.
     cfg = lambda M, N, K, **kw: rs.plan_config(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED, **kw)
     for M in (1, 4, 8):
         c = cfg(M, 16384, 16384)
@@ -322,8 +322,14 @@ def test_plan_config_thin(lib):
         assert cfg(M, 8192, 8192)["engine"] == "mfma"             # 268 MB: measured no faster
     for N in (2, 3, 8):
         c = cfg(16384, N, 16384)
-        assert c["engine"] == "thin" and c["tile"] == (16, N) and c["kchunk"] % 1024 == 0
-        assert cfg(8192, N, 8192)["engine"] == "mfma"
+        # 4-wave workgroups (16 rows) for one or two columns with M >= 16384.
+        assert c["engine"] == "thin" and c["tile"] == (16 if N <= 2 else 32, N) and c["kchunk"] % 1024 == 0
+    assert cfg(16383, 2, 16384)["tile"] == (32, 2) and cfg(65536, 1, 4096)["tile"] == (16, 1)
+    for N in (2, 4):
+        assert cfg(8192, N, 8192)["engine"] == "thin"             # 268 MB, few columns
+        assert cfg(8192, N, 7680)["engine"] == "mfma"             # 252 MB
+    for N in (5, 8):
+        assert cfg(8192, N, 8192)["engine"] == "mfma"             # 268 MB: measured no faster
     assert cfg(8192, 1, 8192)["engine"] == "thin"                 # one column: from 16 MB
     assert cfg(4096, 1, 1024)["engine"] == "thin"
     assert cfg(4096, 1, 1020)["engine"] == "mfma"

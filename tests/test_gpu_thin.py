@@ -62,11 +62,14 @@ def run_thin(ta, tb, M, N, K, alpha, beta, dist, seed):
     return got, ref, S, E, plan
 
 
-# (transa, transb, M, N, K).  The streamed operand is 384 MB or more (16 MB
-# or more for a single column), where the plan takes the thin path.
+# (transa, transb, M, N, K).  The streamed operand is 384 MB or more (256 MB
+# for 2 to 4 columns, 16 MB for a single column), where the plan takes the
+# thin path.  Row counts of the thin_n cases are not multiples of a
+# workgroup's rows (32, or 16 for one or two columns with M >= 16384).
 THIN_M = [(0, 0, 1, 24576, 4096), (1, 0, 3, 16388, 6147), (0, 0, 8, 8196, 12288)]
 THIN_N = [(0, 0, 4096, 1, 1024), (0, 0, 4100, 1, 1028), (0, 1, 16385, 2, 6144), (0, 0, 12289, 5, 8196),
-          (0, 1, 8193, 8, 12288)]
+          (0, 1, 8193, 8, 12288), (0, 0, 8200, 3, 8192), (0, 1, 8210, 4, 8196), (0, 0, 16390, 1, 1028),
+          (0, 1, 16401, 2, 4100)]
 
 
 @pytest.mark.parametrize("case", THIN_M + THIN_N, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
