@@ -283,13 +283,17 @@ ThinPlan thin_plan(const GemmArgs& g) {
     ThinPlan t;
     constexpr int64_t kTarget = 1024, kMinBytes = int64_t(384) << 20;
     constexpr int64_t kMinFewColumns = int64_t(256) << 20, kMinColumn = int64_t(16) << 20;
+    // thin_n's grid has one work-item per 1/16 row (4 rows a wave), which
+    // must stay under the 2^32 work-items a dispatch can count.
+    constexpr int64_t kMaxThinRows = int64_t(1) << 27;
     int64_t groups = 0, min_chunk = 0, quantum = 4;
     const int64_t min_n = g.N == 1 ? kMinColumn : g.N <= 4 ? kMinFewColumns : kMinBytes;
     if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes && rows_vec(g.B, g.ldb, g.N)) {
         t.kind = ThinPlan::THIN_M;
         groups = ceil_div(g.N, 256);
         min_chunk = 256;
-    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= min_n && rows_vec(g.A, g.lda, g.K)) {
+    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= min_n && rows_vec(g.A, g.lda, g.K) &&
+               g.M <= kMaxThinRows) {
         t.kind = ThinPlan::THIN_N;
         t.waves = g.N <= 2 && g.M >= 16384 ? 4 : 8;
         groups = ceil_div(g.M, 4 * t.waves);
