@@ -349,6 +349,7 @@ SMALL_SHAPES = {
     "kheavy1024x1024x4096": (1024, 1024, 4096),
     "skinny64x8192x8192": (64, 8192, 8192),
     "thin1x16384x16384": (1, 16384, 16384),
+    "column16384x1x16384": (16384, 1, 16384),
 }
 
 
