@@ -112,3 +112,32 @@ def test_thin_repeated_calls_identical():
         outs.append(C)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("case", [(0, 0, 2, 16384, 8192), (0, 0, 8192, 3, 8192), (0, 0, 4100, 1, 1028)],
+                         ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+def test_thin_padded_ldc(case):
+    # C with a leading dimension past N: the padding columns and the tail
+    # keep their sentinel; split (workspace, then the reduction) and unsplit
+    # thin calls alike.
+    ta, tb, M, N, K = case
+    A, B = make_operands(M, N, K, "uniform", seed=21)
+    C0 = make_operands(M, 1, N, "uniform", seed=22)[0]
+    Ad, Bd = to_device(A.contiguous()), to_device(B.contiguous())
+    plan = rs.plan_config(M, N, K, A_ptr=Ad.data_ptr(), B_ptr=Bd.data_ptr())
+    note(f"[thin-ldc] {M}x{N}x{K} plan={plan}")
+    assert plan["engine"] == "thin", plan
+    ldc = N + 3
+    Cbuf = torch.full((M * ldc + 16,), 555.0, device="cuda")
+    Cd = torch.as_strided(Cbuf, (M, N), (ldc, 1))
+    Cd.copy_(C0)
+    st = rs.load().sgemm_f32_ex(0, 0, M, N, K, 1.25, Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(),
+                                Bd.stride(0), -0.5, Cbuf.data_ptr(), ldc,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0, rs.status_string(st)
+    torch.cuda.synchronize()
+    full = Cbuf[:M * ldc].view(M, ldc).cpu()
+    assert torch.all(full[:, N:] == 555.0) and torch.all(Cbuf[M * ldc:].cpu() == 555.0), "wrote outside C"
+    ref, S, E = oracle.sgemm_ex_f64(0, 0, 1.25, as_numpy(A), as_numpy(B), -0.5, as_numpy(C0))
+    rep = check.check_ex(full[:, :N].numpy(), ref, S, E, K)
+    assert rep["ok"], rep
