@@ -522,7 +522,20 @@ hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) { return launch_k4
 hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
                                     float* ws) {
     // Occupancy targets as the LDS allows them (2 and 4 workgroups per CU).
-    if (vec_ok(g)) return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4>(g, s, splits, kchunk, ws);
+    // With 16-byte loads, K slabs of 16 in three stages (two slabs in
+    // flight) when a K group's share is short or two workgroups share each
+    // CU: 3-11 % faster than slabs of 32 in two stages on 17 such outputs
+    // (square 256 5.07 -> 4.75 us, 320^3 5.79 -> 5.14, 256^2 x 16384 32.0
+    // -> 31.1, 512 x 256 x 8192 29.9 -> 28.5); alone on a CU with long
+    // shares the extra barriers cost more (64^2 x 65536 22.8 -> 25.3), and
+    // 64 x 64 tiles lose 5-15 % with it.
+    if (vec_ok(g)) {
+        const int64_t share = (splits > 1 ? kchunk : g.K) / 4;
+        const int64_t wgs = ceil_div(g.M, 32) * ceil_div(g.N, 32) * (splits > 1 ? splits : 1);
+        if (share <= 256 || wgs >= 2 * 256)
+            return launch_k4_orient<1, 1, 1, 1, 16, true, 2, true, 3, 4>(g, s, splits, kchunk, ws);
+        return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4>(g, s, splits, kchunk, ws);
+    }
     return launch_k4_orient<1, 1, 1, 1, 16, false, 4, false, 2, 4>(g, s, splits, kchunk, ws);
 }
 

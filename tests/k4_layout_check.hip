@@ -114,6 +114,8 @@ int main() {
     CFG(4, 2, 1, 2, 16)
     CFG(2, 4, 2, 1, 16)
     CFG(4, 2, 1, 2, 32)
+    CFG(2, 2, 2, 4, 16)
+    CFG(1, 1, 1, 1, 32)
     printf("failures: %d\n", failures);
     return failures ? 1 : 0;
 }
