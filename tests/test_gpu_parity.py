@@ -266,3 +266,19 @@ def test_thin_unaligned_auto(shape):
     assert plan["packed"]
     full_check("auto", M, N, K, "uniform", seed=M + N)
     full_check("auto", M, N, K, "int", seed=M + K)
+
+
+# Mid-size outputs of 257 to 768 tiles of 32 x 32 with K <= 1024, which the
+# plan runs unsplit on 32 x 32 tiles with 4 K groups (K slabs of 16 in three
+# LDS stages); edges that are not tile multiples included.
+MID = [(640, 640, 640), (300, 1000, 900), (768, 1024, 1024), (1000, 700, 1000)]
+
+
+@pytest.mark.parametrize("shape", MID, ids=lambda s: "x".join(map(str, s)))
+def test_mid_outputs_auto(shape):
+    M, N, K = shape
+    plan = rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)
+    note(f"[mid] {M}x{N}x{K} plan {plan}")
+    assert plan["tile"] == (32, 32) and plan["k_groups"] == 4 and plan["splits"] == 1, plan
+    full_check("auto", M, N, K, "uniform", seed=M + N)
+    full_check("auto", M, N, K, "int", seed=M + K)
