@@ -220,16 +220,20 @@ static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
     // when a narrow or thin operand is the only unaligned one (8192 x 13 x
     // 8192: 82 -> 61 us; 13 x 8192 x 8191); or 4 GFLOP or more with copies
     // of at most 64 MB and 1 byte per 100 FLOP (767 x 769 x 4095: 91 -> 72
-    // us; 1025 x 1025 x 2047: 78 -> 70).  A copy of 8 to 17 MB takes about
-    // 9 us, so it did not pay below that (1023^3: 32.8 -> 33.2 us; 1024 x
-    // 1027 x 1024: 41.6 -> 42.7), nor where a large operand of a memory-bound
-    // product is copied (1 x 8191 x 8192: 79 -> 144).
+    // us; 1025 x 1025 x 2047: 78 -> 70), or with K >= 1536 from 1 GFLOP
+    // (511 x 513 x 4095: 72 -> 42 us; 800 x 801 x 2047: 48.3 -> 43.3; 767 x
+    // 769 x 2047: 48.1 -> 43.6).  The copy launch and the wait for it cost
+    // about 9 us at 8 MB, so it did not pay for shorter K (1023^3: 32.2 ->
+    // 33.0 us; 1024 x 1027 x 1024: 41.6 -> 42.1; 1023^2 x 511: 19.3 -> 20.7),
+    // nor where a large operand of a memory-bound product is copied (1 x 8191
+    // x 8192: 79 -> 144).
     const double moved = 4.0 * (double(g.M) * g.K + double(g.K) * g.N + double(g.M) * g.N);
     const double flop = 2.0 * double(g.M) * double(g.N) * double(g.K);
     const double copied = double(pk->a_bytes + pk->b_bytes);
     const bool big_output = ceil_div(g.M, 64) * ceil_div(g.N, 64) >= 512;
     const bool thin_copy = moved >= 64e6 && copied <= moved / 8;
-    const bool heavy = flop >= 4e9 && copied <= 64e6 && copied <= flop / 100;
+    const bool heavy = (flop >= 4e9 || (flop >= 1e9 && g.K >= 1536)) && copied <= 64e6 &&
+                       copied <= flop / 100;
     if (!big_output && !thin_copy && !heavy) return false;
     pk->p = k4_plan(gp, 0);
     pk->gp = gp;

@@ -296,6 +296,9 @@ def test_plan_config_choices(lib):
     assert not cfg(1024, 1027, 1024)["packed"] and not cfg(1023, 1023, 1023)["packed"]
     # 4 GFLOP or more with small copies: copied (and split on the copies).
     assert cfg(767, 769, 4095)["packed"] and cfg(513, 511, 8193)["packed"]
+    # 1 GFLOP or more with K >= 1536: copied too; a shorter K is not.
+    assert cfg(511, 513, 4095)["packed"] and cfg(800, 801, 2047)["packed"] and cfg(600, 601, 1600)["packed"]
+    assert not cfg(700, 701, 1500)["packed"] and not cfg(300, 301, 4095)["packed"]
     assert not cfg(64, 64, 1000001)["packed"]      # copies of 512 MB for an 8 GFLOP product
 
 

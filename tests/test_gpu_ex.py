@@ -205,11 +205,13 @@ def test_ex_packed_operands(ta, tb, shape):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("shape", [(767, 769, 4095), (513, 511, 8193), (1025, 1025, 2047)],
+@pytest.mark.parametrize("shape", [(767, 769, 4095), (513, 511, 8193), (1025, 1025, 2047), (511, 513, 4095),
+                                   (600, 601, 1600)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_ex_heavy_mid_size_packed(shape):
     # Mid-size outputs with a long K and unaligned operands: 4 GFLOP or more,
-    # so the plan copies both operands and splits K on the copies.
+    # or 1 GFLOP or more with K >= 1536, so the plan copies both operands and
+    # splits K on the copies.
     M, N, K = shape
     plan = rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)
     print(f"[heavy packed] {M}x{N}x{K} plan {plan}", flush=True)
