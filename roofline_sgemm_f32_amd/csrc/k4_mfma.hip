@@ -371,34 +371,44 @@ hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
 
 // Split-K second pass: C = alpha * (sum of the S partial slabs, added in
 // split order) (+ beta * C when beta is nonzero), the same two roundings the
-// unsplit epilogue applies.  Each lane takes four consecutive columns; VEC
-// (N and ldc multiples of 4, C 16-byte aligned) moves them as one 16-byte
-// access.  W holds S dense M x N slabs.
-template <bool VEC>
+// unsplit epilogue applies.  Each lane takes four consecutive columns.  W
+// holds S slabs of M rows of ldw floats; VW (ldw a multiple of 4, W 16-byte
+// aligned) reads a lane's four partial columns as one 16-byte access, also
+// past N into a row's padding, whose sums are dropped; VC (N and ldc
+// multiples of 4, C 16-byte aligned) moves C the same way.
+template <bool VW, bool VC>
 __global__ void __launch_bounds__(64)
-splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restrict__ C, int64_t ldc,
-              float alpha, float beta) {
+splitk_reduce(int M, int N, int S, const float* __restrict__ W, int64_t ldw, float* __restrict__ C,
+              int64_t ldc, float alpha, float beta) {
     const int nq = (N + 3) / 4;
-    const int64_t total = (int64_t)M * nq, slab = (int64_t)M * N;
+    const int64_t total = (int64_t)M * nq, slab = (int64_t)M * ldw;
     const bool read_c = beta != 0.0f;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int r = (int)(i / nq), c = (int)(i % nq) * 4;
-        const float* w = W + (int64_t)r * N + c;
+        const float* w = W + (int64_t)r * ldw + c;
         float* cp = C + (int64_t)r * ldc + c;
-        if constexpr (VEC) {
+        if constexpr (VW) {
             v4f sum = *(const v4f*)w;
 #pragma unroll 8
             for (int z = 1; z < S; z++) sum += *(const v4f*)(w + z * slab);
             v4f v;
 #pragma unroll
             for (int e = 0; e < 4; e++) v[e] = alpha * sum[e];
-            if (read_c) {
-                const v4f c0 = *(const v4f*)cp;
+            if constexpr (VC) {
+                if (read_c) {
+                    const v4f c0 = *(const v4f*)cp;
 #pragma unroll
-                for (int e = 0; e < 4; e++) v[e] = fmaf(beta, c0[e], v[e]);
+                    for (int e = 0; e < 4; e++) v[e] = fmaf(beta, c0[e], v[e]);
+                }
+                *(v4f*)cp = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if (c + e >= N) break;
+                    cp[e] = read_c ? fmaf(beta, cp[e], v[e]) : v[e];
+                }
             }
-            *(v4f*)cp = v;
         } else {
             for (int e = 0; e < 4 && c + e < N; e++) {
                 float sum = w[e];
@@ -412,34 +422,40 @@ splitk_reduce(int M, int N, int S, const float* __restrict__ W, float* __restric
     }
 }
 
-hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, hipStream_t s) {
+hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, int64_t ldw,
+                                hipStream_t s) {
     const int64_t total = g.M * ceil_div(g.N, 4);
-    const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
+    const bool vw = ldw % 4 == 0 && reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+    const bool vc = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
     // One-wave workgroups: the partial slabs are few and small, so spread
     // them over as many CUs as possible.
     const dim3 grid(grid_for(ceil_div(total, 64)));
-    if (vec)
-        hipLaunchKernelGGL(splitk_reduce<true>, grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
-                           ws, g.C, g.ldc, g.alpha, g.beta);
+    if (vw && vc)
+        hipLaunchKernelGGL((splitk_reduce<true, true>), grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
+                           ws, ldw, g.C, g.ldc, g.alpha, g.beta);
+    else if (vw)
+        hipLaunchKernelGGL((splitk_reduce<true, false>), grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
+                           ws, ldw, g.C, g.ldc, g.alpha, g.beta);
     else
-        hipLaunchKernelGGL(splitk_reduce<false>, grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
-                           ws, g.C, g.ldc, g.alpha, g.beta);
+        hipLaunchKernelGGL((splitk_reduce<false, false>), grid, dim3(64), 0, s, (int)g.M, (int)g.N, splits,
+                           ws, ldw, g.C, g.ldc, g.alpha, g.beta);
     return hipGetLastError();
 }
 
 // K split into `splits` chunks of kchunk (a multiple of BK; every chunk
-// nonempty): partial products into ws (splits x M x N floats), then the
-// reduction into C.
+// nonempty): partial products into ws (splits slabs of M rows of
+// split_ld(N) floats), then the reduction into C.
 template <class CF, int OCC, bool SPLIT = false, int WK = 1>
 hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
+    const int64_t ldw = split_ld(g.N);
     hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true, WK>), dim3(grid_for(tiles), splits),
                        dim3(CF::THREADS * WK), 0, s,
-                       (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, ws, g.N,
+                       (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, ws, ldw,
                        1.0f, 0.0f, (int)tm, (int)tn, (int)tiles, kchunk);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_splitk_reduce(g, splits, ws, s);
+    return launch_splitk_reduce(g, splits, ws, ldw, s);
 }
 
 // The four storage orientations of (A, B) for one tile configuration; with

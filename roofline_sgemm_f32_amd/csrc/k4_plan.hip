@@ -160,7 +160,7 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     if (S <= 1) return {1, g.K, 0, cfg};
     const int64_t kc = ceil_div(ceil_div(g.K, S), bk) * bk;
     S = ceil_div(g.K, kc);
-    return {(int)S, kc, S * g.M * g.N, cfg};
+    return {(int)S, kc, S * g.M * split_ld(g.N), cfg};
 }
 
 static hipError_t launch_plan(const GemmArgs& g, const SplitPlan& p, float* ws, hipStream_t s) {

@@ -80,7 +80,14 @@ PlanInfo plan_info(const GemmArgs& g, int requested);
 hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStream_t s);
 // Split-K second pass: C = alpha * (sum of the `splits` dense M x N slabs of
 // ws, added in slab order) (+ beta * C).
-hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, hipStream_t s);
+// C from `splits` partial slabs in ws, each M rows of ldw floats (C's
+// columns first), added in slab order; alpha and beta as the unsplit
+// epilogue applies them.
+hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, int64_t ldw,
+                                hipStream_t s);
+// Row length of the matrix-core kernel's split partial slabs: N rounded up
+// to 4 floats, so the reduction reads them in 16-byte accesses.
+inline int64_t split_ld(int64_t N) { return (N + 3) / 4 * 4; }
 // Scratch memory for launches that need it: the device's cached buffer,
 // held (with the device's workspace lock) from acquire to release; every
 // launch that uses it goes on stream s in between.

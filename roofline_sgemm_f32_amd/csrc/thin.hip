@@ -269,7 +269,7 @@ hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStrea
         }
     }
     if (e != hipSuccess || p.splits <= 1) return e;
-    return launch_splitk_reduce(g, p.splits, ws, s);
+    return launch_splitk_reduce(g, p.splits, ws, g.N, s);
 }
 
 }  // namespace sgemm
