@@ -120,7 +120,8 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
  * section "Understanding the naive matrix multiplier"): an output of few
  * 64 x 64 tiles leaves most of the 256 compute units idle however long K is.
  * Split-K cuts K into chunks of whole slabs that run as separate workgroups;
- * each stores its partial product to a workspace of (chunks x M x N) floats,
+ * each stores its partial product to a workspace of chunks x M rows of N
+ * floats (rows rounded up to a multiple of 4),
  * and a second kernel adds the partials in chunk order and applies alpha and
  * beta.  The workspace is library memory: one buffer per device, allocated
  * stream-ordered (from a memory pool the library creates) on first need,
