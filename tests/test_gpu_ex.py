@@ -62,8 +62,11 @@ def run_ex(ta, tb, M, N, K, alpha, beta, dist, seed, pad=0, c0_nan=False):
     return got, ref, S, E
 
 
+# With unpadded (16-byte) operands 640 x 576 x 300 runs on 32 x 32 tiles with
+# K groups and 1024 x 960 x 300 on 64 x 64 tiles with K groups, in every
+# orientation; the padded (4-byte) runs take the 32 x 32 configuration.
 SHAPES = [(1, 1, 1), (7, 5, 3), (33, 65, 17), (129, 257, 33), (300, 17, 129), (256, 256, 256),
-          (65, 129, 257), (640, 576, 300)]
+          (65, 129, 257), (640, 576, 300), (1024, 960, 300)]
 COEFS = [(1.0, 0.0), (2.0, 0.5), (-1.5, -2.0), (0.0, 3.0)]
 
 
