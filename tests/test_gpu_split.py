@@ -180,9 +180,10 @@ def test_split_repeated_calls_identical():
 
 
 # One shape per tile configuration of the plan, split on request: 64 x 64
-# tiles with 4 K groups (16-byte loads, under 512 tiles), 32 x 32 with 4 K
-# groups (4-byte loads), 64 x 64 (512 tiles and more), with both load widths.
-CONFIG_SHAPES = [(640, 576, 300), (641, 577, 301), (2048, 1024, 256), (2049, 1023, 255)]
+# tiles with 4 K groups (16-byte loads, under 256 tiles), 32 x 32 with 4 K
+# groups (16-byte loads up to 768 tiles with a short K, and 4-byte loads),
+# 64 x 64 (512 tiles and more), with both load widths.
+CONFIG_SHAPES = [(1024, 960, 300), (640, 576, 300), (641, 577, 301), (2048, 1024, 256), (2049, 1023, 255)]
 
 
 @pytest.mark.parametrize("shape", CONFIG_SHAPES, ids=lambda s: "x".join(map(str, s)))
