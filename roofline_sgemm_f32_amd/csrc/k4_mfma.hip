@@ -10,8 +10,8 @@
 //
 // Structure (geometry and LDS layouts in k4_layout.h):
 //  * a workgroup owns a BM x BN tile of C; each wave TM x TN accumulators;
-//  * K is consumed in slabs of BK through NSTAGE LDS stages (2 in every
-//    configuration used) with one barrier per slab: read this slab's
+//  * K is consumed in slabs of BK through NSTAGE LDS stages (2, or 3 for
+//    the 32 x 32 tiles' slabs of 16) with one barrier per slab: read this slab's
 //    fragments, issue the loads of the slab NSTAGE - 1 ahead, run the slab's
 //    MFMAs, wait for the next slab's loads, barrier;
 //  * global -> LDS uses buffer loads that write LDS directly
@@ -28,7 +28,8 @@
 //    in that XCD's L2;
 //  * options for small outputs: K groups inside the workgroup (WK) and a
 //    split-K mode across workgroups (SPLITK, with a second reduction kernel);
-//    for the largest tiles, raised wave priority during the MFMAs (PRIO).
+//    for the largest tiles, raised wave priority during the MFMAs (PRIO);
+//  * the final C of an unsplit product is stored non-temporally.
 // This file holds the kernel and one launcher per tile configuration; which
 // configuration and split a product gets is decided in k4_plan.hip.
 #include <algorithm>
