@@ -519,8 +519,13 @@ bool vec_ok(const GemmArgs& g) {
 
 hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s) {
     using k4::Cfg;
+    if (vec_ok(g)) {
+        if (!g.trans_a && !g.trans_b) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, true, false>, 2, true, 1, true>(g, s);
+        if (!g.trans_a) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, true, true>, 2, true, 1, true>(g, s);
+        if (!g.trans_b) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, false, false>, 2, true, 1, true>(g, s);
+        return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, false, true>, 2, true, 1, true>(g, s);
+    }
     if (g.trans_a || g.trans_b) return launch_k4_tile128(g, s);
-    if (vec_ok(g)) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true>, 2, true, 1, true>(g, s);
     return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, false>, 2, true, 1, true>(g, s);
 }
 

@@ -42,12 +42,13 @@ namespace sgemm {
 //    40.8) the 64 x 64 choice stays.
 //  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
 //    SIMD, fragments read in halves, raised wave priority during the
-//    matrix instructions) for A and B as stored (no transposes) when the
-//    tiles fill whole rounds of 2 per CU, or the last round at least 3/4:
-//    square 4096 0.956 ms against 0.990 on 128 x 128, 8192 7.57 against
-//    7.79 ms, 5632 2.63 against 2.71; with a smaller last round (square
-//    3072, 4608, 6144) it is the slowest of the three, and with B stored
-//    transposed 128 x 128 is as fast.
+//    matrix instructions) when the tiles fill whole rounds of 2 per CU, or
+//    the last round at least 3/4: square 4096 0.956 ms against 0.990 on
+//    128 x 128, 8192 7.57 against 7.79 ms, 5632 2.63 against 2.71; with a
+//    smaller last round (square 3072, 4608, 6144) it is the slowest of the
+//    three.  Stored transposes take it too (square 8192 with B stored N x K
+//    8.11 -> 7.68 ms, A stored K x M 7.90 -> 7.74; square 4096 with A stored
+//    K x M 1.006 -> 0.980; both transposed within 0.3 %).
 
 // Split-K on top of the tile choice, when the tiles alone leave the chip
 // underused (same sweeps, timed as back-to-back calls so that the second
@@ -122,7 +123,7 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     const double area = double(g.M) * double(g.N);
     const bool full256 = area >= 0.875 * double(T256) * 128.0 * 256.0;
     const bool full128 = area >= 0.875 * double(T128) * 128.0 * 128.0;
-    if (vec && !g.trans_a && !g.trans_b && full256 && T256 >= 512 &&
+    if (vec && full256 && T256 >= 512 &&
         (T256 % 512 == 0 || T256 % 512 >= 384)) {
         cfg = K4_T128X256;
         tiles = T256;

@@ -268,7 +268,8 @@ def test_plan_config_choices(lib):
     assert big == {"engine": "mfma", "tile": (128, 256), "k_groups": 1, "packed": False, "splits": 1,
                    "kchunk": 4096}
     assert cfg(8192, 8192, 8192)["tile"] == (128, 256)
-    assert cfg(4096, 4096, 4096, transb=True)["tile"] == (128, 128)   # 128 x 256 needs A, B as stored
+    for ta, tb in [(True, False), (False, True), (True, True)]:      # every storage orientation
+        assert cfg(4096, 4096, 4096, transa=ta, transb=tb, lda=4096, ldb=4096)["tile"] == (128, 256)
     assert cfg(6144, 6144, 6144)["tile"] == (128, 128)               # 2.25 rounds of 128 x 256
     assert cfg(3072, 3072, 3072)["tile"] == (64, 64)
     assert cfg(1024, 1024, 1024)["tile"] == (64, 64) and cfg(1024, 1024, 1024)["k_groups"] == 4

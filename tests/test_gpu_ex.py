@@ -190,6 +190,23 @@ def test_ex_square4096_sampled(ta, tb):
     assert check.check(Cn[:, cols], ref, S, w.K)["ok"]
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)], ids=["NN", "NT", "TN", "TT"])
+def test_ex_128x256_every_orientation(ta, tb):
+    # 512 tiles of 128 x 256 with a short K: the largest tiles in each storage
+    # orientation, every element against the oracle, integer-exact and
+    # uniform with alpha, beta.
+    M, N, K = 2048, 8192, 72
+    plan = rs.plan_config(M, N, K, transa=bool(ta), transb=bool(tb), lda=M if ta else K,
+                          ldb=K if tb else N, A_ptr=1 << 40, B_ptr=1 << 40)
+    print(f"[ex128x256] {ta}{tb} plan {plan}", flush=True)
+    assert plan["tile"] == (128, 256), plan
+    got, ref, _, _ = run_ex(ta, tb, M, N, K, 1.0, 0.0, "int", seed=11)
+    assert np.array_equal(got.astype(np.float64), ref)
+    got, ref, S, E = run_ex(ta, tb, M, N, K, -0.75, 1.5, "uniform", seed=12)
+    rep = check.check_ex(got, ref, S, E, K)
+    assert rep["ok"], rep
+
+
 # Outputs large enough for 64 x 64 tiles whose operands do not suit 16-byte
 # loads are packed into zero-padded aligned copies first: both operands, only
 # A (K odd), only B (N odd), in every orientation.
