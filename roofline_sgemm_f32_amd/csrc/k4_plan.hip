@@ -290,7 +290,7 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
 // 4096 300 -> 274, 65536 x 2 x 4096 204 -> 181, 16384 x 1 x 16384 168 ->
 // 162).  K is split so that about 1024 workgroups keep loads in flight; a
 // chunk keeps at least 256 of K (thin_m) or one 1024-k piece (thin_n).
-ThinPlan thin_plan(const GemmArgs& g) {
+static ThinPlan thin_plan_direct(const GemmArgs& g, bool transposed) {
     ThinPlan t;
     constexpr int64_t kTarget = 1024, kMinBytes = int64_t(384) << 20;
     constexpr int64_t kMinFewColumns = int64_t(256) << 20, kMinColumn = int64_t(16) << 20;
@@ -298,7 +298,11 @@ ThinPlan thin_plan(const GemmArgs& g) {
     // must stay under the 2^32 work-items a dispatch can count.
     constexpr int64_t kMaxThinRows = int64_t(1) << 27;
     int64_t groups = 0, min_chunk = 0, quantum = 4;
-    const int64_t min_n = g.N == 1 ? kMinColumn : g.N <= 4 ? kMinFewColumns : kMinBytes;
+    // The lower thresholds for few columns are where the matrix-core path
+    // reads the small operand with 4-byte loads; a transposed product's
+    // original keeps 16-byte loads there (1 x 8192 x 8192 with B stored N x K:
+    // 48.7 us on the matrix cores, 50.0 on thin_n).
+    const int64_t min_n = transposed ? kMinBytes : g.N == 1 ? kMinColumn : g.N <= 4 ? kMinFewColumns : kMinBytes;
     if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes && rows_vec(g.B, g.ldb, g.N)) {
         t.kind = ThinPlan::THIN_M;
         groups = ceil_div(g.N, 256);
@@ -322,14 +326,32 @@ ThinPlan thin_plan(const GemmArgs& g) {
     return t;
 }
 
+// A large operand stored with K contiguous on the other side (B stored
+// N x K with M <= 8, A stored K x M with N <= 8) is streamed by the same
+// kernels on the transposed product, whose result they store transposed,
+// from 384 MB (MI355X, us: 1 x 16384 x 16384 with B stored N x K 268 ->
+// 167, 16384 x 1 x 16384 with A stored K x M 290 -> 164, 8 x 16384 x 16384
+// 270 -> 207, 16384 x 8 x 16384 286 -> 184, 2 x 65536 x 4096 265 -> 187).
+ThinPlan thin_plan(const GemmArgs& g) {
+    ThinPlan t = thin_plan_direct(g, false);
+    if (t.kind != ThinPlan::NONE || (g.M > 8 && g.N > 8)) return t;
+    t = thin_plan_direct(swapped(g), true);
+    t.swap = t.kind != ThinPlan::NONE;
+    return t;
+}
+
 PlanInfo plan_info(const GemmArgs& g, int requested) {
     PlanInfo info;
     if (requested == 0) {
         const ThinPlan t = thin_plan(g);
         if (t.kind != ThinPlan::NONE) {
             info.engine = 2;
-            info.tile_m = t.kind == ThinPlan::THIN_M ? (int)g.M : 4 * t.waves;
-            info.tile_n = t.kind == ThinPlan::THIN_M ? 256 : (int)g.N;
+            const GemmArgs gt = t.swap ? swapped(g) : g;
+            int tm = t.kind == ThinPlan::THIN_M ? (int)gt.M : 4 * t.waves;
+            int tn = t.kind == ThinPlan::THIN_M ? 256 : (int)gt.N;
+            if (t.swap) std::swap(tm, tn);
+            info.tile_m = tm;
+            info.tile_n = tn;
             info.k_groups = t.kind == ThinPlan::THIN_M ? 4 : 1;
             info.splits = t.splits;
             info.kchunk = t.kchunk;

@@ -58,12 +58,31 @@ SplitPlan k4_plan(const GemmArgs& g, int requested_splits);
 // Thin products on the vector units (thin.hip): M <= 8 (B streamed) or
 // N <= 8 (A streamed), in `splits` K chunks of kchunk whose partial
 // products take ws_floats floats of workspace; thin_n workgroups of `waves`
-// waves (8, or 4 for N <= 2), 4 rows of C each.
+// waves (8, or 4 for N <= 2), 4 rows of C each.  swap: the plan is for the
+// transposed product C^T = op(B)^T op(A)^T (swapped(g)), whose kernels store
+// C^T into C transposed; that is how a large operand stored with K
+// contiguous on the other side (B stored N x K for M <= 8, A stored K x M
+// for N <= 8) is streamed.
 struct ThinPlan {
     enum Kind { NONE, THIN_M, THIN_N } kind = NONE;
     int splits = 1, waves = 8;
+    bool swap = false;
     int64_t kchunk = 0, ws_floats = 0;
 };
+// The transposed product C^T = op(B)^T op(A)^T, with C^T held in C (its
+// element (j, i) at C[i * ldc + j]).
+inline GemmArgs swapped(const GemmArgs& g) {
+    GemmArgs t = g;
+    t.M = g.N;
+    t.N = g.M;
+    t.A = g.B;
+    t.lda = g.ldb;
+    t.trans_a = !g.trans_b;
+    t.B = g.A;
+    t.ldb = g.lda;
+    t.trans_b = !g.trans_a;
+    return t;
+}
 // Whether a shape-chosen call takes the thin path, and how.
 ThinPlan thin_plan(const GemmArgs& g);
 // What an eager call with this K-split request runs (requested 0: shape-

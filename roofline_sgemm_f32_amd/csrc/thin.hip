@@ -37,12 +37,15 @@ constexpr int kThinMUnroll = 8;     // rows of B in flight per lane (16 B each)
 constexpr int kThinNRows = 4;       // rows of A (and C) per wave in thin_n
 constexpr int kThinNPiece = 1024;   // k per LDS piece of B in thin_n
 
-// Store one row segment of C from a lane: alpha * v (+ beta * C).
-__device__ __forceinline__ void store_c(float* c, const float* v, int n, float alpha, float beta) {
+// Store n values of C from a lane, element e at c[e * step]: alpha * v
+// (+ beta * C).  step 1 stores a row segment; step ldc stores it into a
+// column of C, where a transposed product keeps its result.
+__device__ __forceinline__ void store_c(float* c, int64_t step, const float* v, int n, float alpha,
+                                        float beta) {
     for (int e = 0; e < n; e++) {
         float r = alpha * v[e];
-        if (beta != 0.0f) r = fmaf(beta, c[e], r);
-        c[e] = r;
+        if (beta != 0.0f) r = fmaf(beta, c[e * step], r);
+        c[e * step] = r;
     }
 }
 }  // namespace
@@ -53,7 +56,7 @@ template <int MR, bool TA>
 __global__ void __launch_bounds__(kThinThreads)
 thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
        const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
-       float alpha, float beta) {
+       float alpha, float beta, bool tc) {
     __shared__ v4f red[3][64][MR];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n0 = (blockIdx.x * 64 + lane) * 4;
@@ -111,7 +114,10 @@ thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
 #pragma unroll
         for (int m = 0; m < MR; m++) {
             const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
-            store_c(out + (int64_t)m * ldo + n0, v, 4, alpha, beta);
+            if (tc)
+                store_c(out + (int64_t)n0 * ldo + m, ldo, v, 4, alpha, beta);
+            else
+                store_c(out + (int64_t)m * ldo + n0, 1, v, 4, alpha, beta);
         }
     }
 }
@@ -123,7 +129,7 @@ template <int NR, bool TB, int WAVES, int UN>
 __global__ void __launch_bounds__(64 * WAVES)
 thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
        const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
-       float alpha, float beta) {
+       float alpha, float beta, bool tc) {
     // B piece, k-major per column; the pad keeps the 16-byte reads of one
     // column's k run conflict-free across columns.
     __shared__ __attribute__((aligned(16))) float bs[NR][kThinNPiece + 4];
@@ -194,65 +200,92 @@ thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
 #pragma unroll
             for (int n = 0; n < NR; n++) o[n] = acc[r][n];
         } else {
-            store_c(out + (int64_t)(row0 + r) * ldo, acc[r], NR, alpha, beta);
+            if (tc)
+                store_c(out + (row0 + r), ldo, acc[r], NR, alpha, beta);
+            else
+                store_c(out + (int64_t)(row0 + r) * ldo, 1, acc[r], NR, alpha, beta);
         }
     }
 }
 
 namespace {
 template <int MR>
-hipError_t launch_thin_m_r(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
+hipError_t launch_thin_m_r(const GemmArgs& g, int splits, int kchunk, float* ws, bool tc, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(g.N, 256), (unsigned)splits);
     float* out = splits > 1 ? ws : g.C;
     const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
     if (g.trans_a)
         hipLaunchKernelGGL((thin_m<MR, true>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
-                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
     else
         hipLaunchKernelGGL((thin_m<MR, false>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
-                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
     return hipGetLastError();
 }
 
 template <int NR, int WAVES, int UN>
-void launch_thin_n_w(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
+void launch_thin_n_w(const GemmArgs& g, int splits, int kchunk, float* ws, bool tc, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(g.M, WAVES * kThinNRows), (unsigned)splits);
     float* out = splits > 1 ? ws : g.C;
     const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
     if (g.trans_b)
         hipLaunchKernelGGL((thin_n<NR, true, WAVES, UN>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
-                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
     else
         hipLaunchKernelGGL((thin_n<NR, false, WAVES, UN>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
-                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta);
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
 }
 
 template <int NR>
 hipError_t launch_thin_n_r(const GemmArgs& g, const ThinPlan& p, float* ws, hipStream_t s) {
     if constexpr (NR <= 2) {
         if (p.waves == 4) {
-            launch_thin_n_w<NR, 4, 1>(g, p.splits, (int)p.kchunk, ws, s);
+            launch_thin_n_w<NR, 4, 1>(g, p.splits, (int)p.kchunk, ws, p.swap, s);
             return hipGetLastError();
         }
     }
     if (p.waves != 8) return hipErrorInvalidValue;
-    launch_thin_n_w<NR, 8, 2>(g, p.splits, (int)p.kchunk, ws, s);
+    launch_thin_n_w<NR, 8, 2>(g, p.splits, (int)p.kchunk, ws, p.swap, s);
     return hipGetLastError();
+}
+
+// Split reduction of a transposed thin product: the partial slabs hold the
+// M x N product dense (M x N of the transposed problem), and element (r, j)
+// of their sum goes to C[j * ldc + r]; lanes run along r, so C is written
+// in runs of consecutive floats.  Slabs are added in order, alpha and beta
+// applied as in splitk_reduce.
+__global__ void __launch_bounds__(256)
+thin_reduce_t(int M, int N, int S, const float* __restrict__ W, float* __restrict__ C, int64_t ldc,
+              float alpha, float beta) {
+    const int64_t total = (int64_t)M * N, slab = total;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = i / M, r = i % M;
+        const float* w = W + r * N + j;
+        float sum = w[0];
+        for (int z = 1; z < S; z++) sum += w[z * slab];
+        float v = alpha * sum;
+        float* c = C + j * ldc + r;
+        if (beta != 0.0f) v = fmaf(beta, *c, v);
+        *c = v;
+    }
 }
 }  // namespace
 
-hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStream_t s) {
+hipError_t launch_thin(const GemmArgs& g0, const ThinPlan& p, float* ws, hipStream_t s) {
+    // A swapped plan runs the transposed product, stored transposed.
+    const GemmArgs g = p.swap ? swapped(g0) : g0;
     hipError_t e;
     if (p.kind == ThinPlan::THIN_M) {
         switch (g.M) {
-            case 1: e = launch_thin_m_r<1>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 2: e = launch_thin_m_r<2>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 3: e = launch_thin_m_r<3>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 4: e = launch_thin_m_r<4>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 5: e = launch_thin_m_r<5>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 6: e = launch_thin_m_r<6>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 7: e = launch_thin_m_r<7>(g, p.splits, (int)p.kchunk, ws, s); break;
-            case 8: e = launch_thin_m_r<8>(g, p.splits, (int)p.kchunk, ws, s); break;
+            case 1: e = launch_thin_m_r<1>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 2: e = launch_thin_m_r<2>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 3: e = launch_thin_m_r<3>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 4: e = launch_thin_m_r<4>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 5: e = launch_thin_m_r<5>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 6: e = launch_thin_m_r<6>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 7: e = launch_thin_m_r<7>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
+            case 8: e = launch_thin_m_r<8>(g, p.splits, (int)p.kchunk, ws, p.swap, s); break;
             default: return hipErrorInvalidValue;
         }
     } else {
@@ -269,7 +302,11 @@ hipError_t launch_thin(const GemmArgs& g, const ThinPlan& p, float* ws, hipStrea
         }
     }
     if (e != hipSuccess || p.splits <= 1) return e;
-    return launch_splitk_reduce(g, p.splits, ws, g.N, s);
+    if (!p.swap) return launch_splitk_reduce(g, p.splits, ws, g.N, s);
+    const int64_t total = g.M * g.N;
+    hipLaunchKernelGGL(thin_reduce_t, dim3(grid_for(ceil_div(total, 256))), dim3(256), 0, s, (int)g.M,
+                       (int)g.N, p.splits, ws, g.C, g.ldc, g.alpha, g.beta);
+    return hipGetLastError();
 }
 
 }  // namespace sgemm

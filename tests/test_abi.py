@@ -348,8 +348,15 @@ def test_plan_config_thin(lib):
     assert cfg(4096, 1, 1020)["engine"] == "mfma"
     assert cfg(16384, 8, 16384, transb=True)["engine"] == "thin"  # B is staged, any orientation
     assert cfg(8, 16384, 16384, transa=True)["engine"] == "thin"  # A read by scalar loads
-    assert cfg(16384, 8, 16384, transa=True)["engine"] == "mfma"  # the streamed side must be row-major
-    assert cfg(8, 16384, 16384, transb=True)["engine"] == "mfma"
+    # A streamed operand stored with K contiguous on the other side: the
+    # transposed product on the same kernels, stored transposed.
+    c = cfg(16384, 8, 16384, transa=True, lda=16384)
+    assert c["engine"] == "thin" and c["tile"] == (256, 8) and c["k_groups"] == 4
+    c = cfg(8, 16384, 16384, transb=True, ldb=16384)
+    assert c["engine"] == "thin" and c["tile"] == (8, 32)
+    assert cfg(1, 16384, 16384, transb=True, ldb=16384)["tile"] == (1, 16)
+    assert cfg(1, 8192, 8192, transb=True, ldb=8192)["engine"] == "mfma"   # from 384 MB when transposed
+    assert cfg(16384, 8, 16384, transa=True, lda=16385)["engine"] == "mfma"  # rows not 16-byte chunks
     assert cfg(16, 16384, 16384)["engine"] == "mfma"              # not thin
     assert cfg(1, 16383, 16384)["engine"] == "mfma"               # B rows not 16-byte chunks
     assert cfg(16384, 1, 16383)["engine"] == "mfma"               # A rows not 16-byte chunks

@@ -70,9 +70,15 @@ THIN_M = [(0, 0, 1, 24576, 4096), (1, 0, 3, 16388, 6147), (0, 0, 8, 8196, 12288)
 THIN_N = [(0, 0, 4096, 1, 1024), (0, 0, 4100, 1, 1028), (0, 1, 16385, 2, 6144), (0, 0, 12289, 5, 8196),
           (0, 1, 8193, 8, 12288), (0, 0, 8200, 3, 8192), (0, 1, 8210, 4, 8196), (0, 0, 16390, 1, 1028),
           (0, 1, 16401, 2, 4100)]
+# The large operand stored with K contiguous on the other side (B stored
+# N x K with M <= 8, A stored K x M with N <= 8, 384 MB or more): the
+# transposed product on the thin kernels, stored transposed, split
+# (reduction into C transposed) and whole.
+THIN_T = [(0, 1, 1, 24576, 4096), (1, 1, 5, 16388, 6148), (1, 0, 98308, 1, 1028), (1, 0, 16392, 2, 8192),
+          (1, 1, 12292, 7, 8200)]
 
 
-@pytest.mark.parametrize("case", THIN_M + THIN_N, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+@pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
 def test_thin_uniform(case):
     ta, tb, M, N, K = case
     for alpha, beta in [(1.0, 0.0), (-1.5, 0.75)]:
@@ -81,7 +87,7 @@ def test_thin_uniform(case):
         assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("case", THIN_M + THIN_N, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+@pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
 def test_thin_integer_exact(case):
     ta, tb, M, N, K = case
     for alpha, beta in [(1.0, 0.0), (2.0, -1.0)]:
@@ -141,3 +147,33 @@ def test_thin_padded_ldc(case):
     ref, S, E = oracle.sgemm_ex_f64(0, 0, 1.25, as_numpy(A), as_numpy(B), -0.5, as_numpy(C0))
     rep = check.check_ex(full[:, :N].numpy(), ref, S, E, K)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("case", [(0, 1, 2, 16384, 8192), (1, 0, 16392, 3, 8192)],
+                         ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+def test_thin_transposed_padded_ldc(case):
+    # A transposed thin product stores C transposed: into a C whose leading
+    # dimension is past N, leaving the padding and the tail untouched.
+    ta, tb, M, N, K = case
+    A, B = make_operands(M, N, K, "int", seed=31)
+    C0 = make_operands(M, 1, N, "int", seed=32)[0]
+    As = A.t().contiguous() if ta else A.contiguous()
+    Bs = B.t().contiguous() if tb else B.contiguous()
+    Ad, Bd = to_device(As), to_device(Bs)
+    plan = rs.plan_config(M, N, K, transa=bool(ta), transb=bool(tb), lda=Ad.stride(0), ldb=Bd.stride(0),
+                          A_ptr=Ad.data_ptr(), B_ptr=Bd.data_ptr())
+    note(f"[thin-t-ldc] {ta}{tb} {M}x{N}x{K} plan={plan}")
+    assert plan["engine"] == "thin", plan
+    ldc = N + 3
+    Cbuf = torch.full((M * ldc + 16,), 555.0, device="cuda")
+    Cd = torch.as_strided(Cbuf, (M, N), (ldc, 1))
+    Cd.copy_(C0)
+    st = rs.load().sgemm_f32_ex(ta, tb, M, N, K, 2.0, Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(),
+                                Bd.stride(0), -1.0, Cbuf.data_ptr(), ldc,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0, rs.status_string(st)
+    torch.cuda.synchronize()
+    full = Cbuf[:M * ldc].view(M, ldc).cpu()
+    assert torch.all(full[:, N:] == 555.0) and torch.all(Cbuf[M * ldc:].cpu() == 555.0), "wrote outside C"
+    ref, _, _ = oracle.sgemm_ex_f64(ta, tb, 2.0, as_numpy(As), as_numpy(Bs), -1.0, as_numpy(C0))
+    assert np.array_equal(full[:, :N].numpy().astype(np.float64), ref)
