@@ -275,8 +275,11 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
 }
 
 // Thin products (one side of C at most 8) stream their large operand on the
-// vector units (thin.hip) when it suits 16-byte loads (B stored K x N for
-// M <= 8, A stored M x K for N <= 8) and is large enough: 384 MB or more;
+// vector units (thin.hip) when it is stored with K on the long axis (B
+// stored K x N for M <= 8 in whole 16-byte row chunks; A stored M x K for
+// N <= 8, in 16-byte or, for rows that are not whole chunks, 4-byte loads:
+// 16384 x 1 x 16383 314 -> 176 us, 65536 x 2 x 4095 689 -> 183, against the
+// matrix cores' 4-byte path) and is large enough: 384 MB or more;
 // for N <= 4, 256 MB; for a single column, 16 MB.  Measured against the
 // matrix-core path, whose 32 x 32 tiles stream the operand too (MI355X,
 // back-to-back launches, us): 1 x 16384 x 16384 290 -> 168, 16384 x 8 x
@@ -307,8 +310,7 @@ static ThinPlan thin_plan_direct(const GemmArgs& g, bool transposed) {
         t.kind = ThinPlan::THIN_M;
         groups = ceil_div(g.N, 256);
         min_chunk = 256;
-    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= min_n && rows_vec(g.A, g.lda, g.K) &&
-               g.M <= kMaxThinRows) {
+    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= min_n && g.M <= kMaxThinRows) {
         t.kind = ThinPlan::THIN_N;
         t.waves = g.N <= 2 && g.M >= 16384 ? 4 : 8;
         groups = ceil_div(g.M, 4 * t.waves);

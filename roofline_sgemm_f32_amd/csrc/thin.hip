@@ -122,10 +122,10 @@ thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
     }
 }
 
-// out as in thin_m (ldo = ldc, or N for the workspace).  K % 4 == 0, A's
-// rows 16-byte aligned.  B element (k, n) is B[k * ldb + n], or
-// B[n * ldb + k] when TB.
-template <int NR, bool TB, int WAVES, int UN>
+// out as in thin_m (ldo = ldc, or N for the workspace).  VA: K % 4 == 0 and
+// A's rows 16-byte aligned (16-byte loads); otherwise 4-byte loads.  B
+// element (k, n) is B[k * ldb + n], or B[n * ldb + k] when TB.
+template <int NR, bool TB, int WAVES, int UN, bool VA>
 __global__ void __launch_bounds__(64 * WAVES)
 thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
        const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
@@ -157,6 +157,37 @@ thin_n(int M, int K, int kchunk, const float* __restrict__ A, int64_t lda,
             bs[n][k] = TB ? B[(int64_t)n * ldb + p0 + k] : B[(int64_t)(p0 + k) * ldb + n];
         }
         __syncthreads();
+        if constexpr (!VA) {
+            // Rows of A not in 16-byte chunks: 4-byte loads, lane takes
+            // k = p0 + lane + 64 q + 256 t (q < 4), each load 256 contiguous
+            // bytes across the wave; any pk.
+            for (int kb = 0; kb < pk; kb += 256 * UN) {
+                float a[UN][kThinNRows][4];
+#pragma unroll
+                for (int u = 0; u < UN; u++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const int kk = kb + 256 * u + 64 * q + lane;
+#pragma unroll
+                        for (int r = 0; r < kThinNRows; r++)
+                            a[u][r][q] = live[r] && kk < pk ? __builtin_nontemporal_load(ap[r] + p0 + kk) : 0.0f;
+                    }
+#pragma unroll
+                for (int u = 0; u < UN; u++) {
+                    const int kk = kb + 256 * u + lane;
+#pragma unroll
+                    for (int n = 0; n < NR; n++) {
+                        float b[4];
+#pragma unroll
+                        for (int q = 0; q < 4; q++) b[q] = kk + 64 * q < pk ? bs[n][kk + 64 * q] : 0.0f;
+#pragma unroll
+                        for (int r = 0; r < kThinNRows; r++)
+                            acc[r][n] += a[u][r][0] * b[0] + a[u][r][1] * b[1] + a[u][r][2] * b[2] + a[u][r][3] * b[3];
+                    }
+                }
+            }
+            continue;
+        }
         // Lane takes k = p0 + 4 lane + 256 t, UN steps t per batch with all
         // their loads issued first.  pk is a multiple of 4.
         for (int kb = 0; kb < pk; kb += 256 * UN) {
@@ -228,11 +259,18 @@ void launch_thin_n_w(const GemmArgs& g, int splits, int kchunk, float* ws, bool 
     const dim3 grid((unsigned)ceil_div(g.M, WAVES * kThinNRows), (unsigned)splits);
     float* out = splits > 1 ? ws : g.C;
     const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
-    if (g.trans_b)
-        hipLaunchKernelGGL((thin_n<NR, true, WAVES, UN>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
+    const bool va = rows_vec(g.A, g.lda, g.K);
+    if (g.trans_b && va)
+        hipLaunchKernelGGL((thin_n<NR, true, WAVES, UN, true>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
+    else if (va)
+        hipLaunchKernelGGL((thin_n<NR, false, WAVES, UN, true>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
+    else if (g.trans_b)
+        hipLaunchKernelGGL((thin_n<NR, true, WAVES, UN, false>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
                            kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
     else
-        hipLaunchKernelGGL((thin_n<NR, false, WAVES, UN>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
+        hipLaunchKernelGGL((thin_n<NR, false, WAVES, UN, false>), grid, dim3(64 * WAVES), 0, s, (int)g.M, (int)g.K,
                            kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
 }
 

@@ -75,10 +75,12 @@ THIN_N = [(0, 0, 4096, 1, 1024), (0, 0, 4100, 1, 1028), (0, 1, 16385, 2, 6144), 
 # transposed product on the thin kernels, stored transposed, split
 # (reduction into C transposed) and whole.
 THIN_T = [(0, 1, 1, 24576, 4096), (1, 1, 5, 16388, 6148), (1, 0, 98308, 1, 1028), (1, 0, 16392, 2, 8192),
-          (1, 1, 12292, 7, 8200)]
+          (1, 1, 12292, 7, 8200), (0, 1, 1, 24576, 4097)]
+# A's rows not in 16-byte chunks (K odd): thin_n with 4-byte loads.
+THIN_U = [(0, 0, 16384, 1, 16383), (0, 1, 12289, 3, 8191), (0, 0, 100003, 4, 1023)]
 
 
-@pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+@pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T + THIN_U, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
 def test_thin_uniform(case):
     ta, tb, M, N, K = case
     for alpha, beta in [(1.0, 0.0), (-1.5, 0.75)]:
@@ -87,7 +89,7 @@ def test_thin_uniform(case):
         assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
+@pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T + THIN_U, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
 def test_thin_integer_exact(case):
     ta, tb, M, N, K = case
     for alpha, beta in [(1.0, 0.0), (2.0, -1.0)]:
