@@ -359,7 +359,7 @@ def test_plan_config_thin(lib):
     assert cfg(16384, 8, 16384, transa=True, lda=16385)["engine"] == "mfma"  # rows not 16-byte chunks
     assert cfg(16, 16384, 16384)["engine"] == "mfma"              # not thin
     assert cfg(1, 16383, 16384)["engine"] == "mfma"               # B rows not 16-byte chunks
-    assert cfg(16384, 1, 16383)["engine"] == "mfma"               # A rows not 16-byte chunks
+    assert cfg(16384, 1, 16383)["engine"] == "thin"               # A rows not 16-byte chunks: 4-byte loads
     assert cfg(1 << 27, 1, 4)["engine"] == "thin"                 # rows the thin_n grid can count
     assert cfg((1 << 27) + 4, 1, 4)["engine"] == "mfma"
     # A split request bypasses the thin path.
