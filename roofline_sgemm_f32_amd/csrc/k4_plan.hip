@@ -276,10 +276,10 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
 
 // Thin products (one side of C at most 8) stream their large operand on the
 // vector units (thin.hip) when it is stored with K on the long axis (B
-// stored K x N for M <= 8 in whole 16-byte row chunks; A stored M x K for
-// N <= 8, in 16-byte or, for rows that are not whole chunks, 4-byte loads:
-// 16384 x 1 x 16383 314 -> 176 us, 65536 x 2 x 4095 689 -> 183, against the
-// matrix cores' 4-byte path) and is large enough: 384 MB or more;
+// stored K x N for M <= 8, A stored M x K for N <= 8; in 16-byte loads, or
+// 4-byte ones for rows that are not whole 16-byte chunks: 16384 x 1 x 16383
+// 314 -> 176 us, 2 x 65535 x 4096 698 -> 178, against the matrix cores'
+// 4-byte path) and is large enough: 384 MB or more;
 // for N <= 4, 256 MB; for a single column, 16 MB.  Measured against the
 // matrix-core path, whose 32 x 32 tiles stream the operand too (MI355X,
 // back-to-back launches, us): 1 x 16384 x 16384 290 -> 168, 16384 x 8 x
@@ -306,7 +306,7 @@ static ThinPlan thin_plan_direct(const GemmArgs& g, bool transposed) {
     // original keeps 16-byte loads there (1 x 8192 x 8192 with B stored N x K:
     // 48.7 us on the matrix cores, 50.0 on thin_n).
     const int64_t min_n = transposed ? kMinBytes : g.N == 1 ? kMinColumn : g.N <= 4 ? kMinFewColumns : kMinBytes;
-    if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes && rows_vec(g.B, g.ldb, g.N)) {
+    if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes) {
         t.kind = ThinPlan::THIN_M;
         groups = ceil_div(g.N, 256);
         min_chunk = 256;

@@ -9,12 +9,15 @@
 // large operand in 16-byte loads along its contiguous dimension, one pass,
 // and keep the small one close:
 //  * thin_m (M <= 8, B stored K x N): lane owns 4 columns of C; a wave's
-//    loads of one row of B are 1 KB contiguous; the M values of A a step
+//    loads of one row of B are 1 KB contiguous (four 256-byte runs of 4-byte
+//    loads when B's rows are not whole 16-byte chunks); the M values of A a step
 //    needs are the same for every lane (scalar loads).  The workgroup's four
 //    waves take four consecutive K ranges of the chunk and add their partial
 //    columns in wave order through LDS.
 //  * thin_n (N <= 8, A stored M x K): a wave owns 4 rows of C and its lanes
-//    split K, 4 consecutive k per lane per step, UN steps' loads in flight;
+//    split K, 4 consecutive k per lane per step (or 4 k 64 apart, with
+//    4-byte loads, when A's rows are not whole 16-byte chunks), UN steps'
+//    loads in flight;
 //    the workgroup (WAVES waves: 8 with UN 2, or 4 with UN 1 for long A of
 //    one or two columns) stages B (K x N or N x K) through LDS, k-major per
 //    column, in pieces of 1024 k.  Lane partial sums are added by a fixed
@@ -51,15 +54,29 @@ __device__ __forceinline__ void store_c(float* c, int64_t step, const float* v, 
 }  // namespace
 
 // out: C (ldo = ldc) when slab == 0, else the workspace, chunk z at
-// out + z * slab with ldo = N.  N % 4 == 0, B's rows 16-byte aligned.
-template <int MR, bool TA>
+// out + z * slab with ldo = N.  VB: N % 4 == 0 and B's rows 16-byte
+// aligned, a lane's four columns consecutive (one 16-byte load per row);
+// otherwise they are 64 apart (four 4-byte loads, each wave instruction
+// still 256 contiguous bytes) and any N.
+template <int MR, bool TA, bool VB>
 __global__ void __launch_bounds__(kThinThreads)
 thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
        const float* __restrict__ B, int64_t ldb, float* __restrict__ out, int64_t ldo, int64_t slab,
        float alpha, float beta, bool tc) {
     __shared__ v4f red[3][64][MR];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n0 = (blockIdx.x * 64 + lane) * 4;
+    // Column of the lane's component e.
+    auto col = [&](int e) { return VB ? (blockIdx.x * 64 + lane) * 4 + e : blockIdx.x * 256 + lane + 64 * e; };
+    auto load_row = [&](const float* rowp) -> v4f {
+        if constexpr (VB) {
+            return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(rowp + col(0)));
+        } else {
+            v4f b;
+#pragma unroll
+            for (int e = 0; e < 4; e++) b[e] = col(e) < N ? __builtin_nontemporal_load(rowp + col(e)) : 0.0f;
+            return b;
+        }
+    };
     const int z = blockIdx.y;
     const int kc0 = z * kchunk, kc1 = min(K, kc0 + kchunk);
     // Wave w takes the w-th quarter of the chunk.
@@ -68,14 +85,13 @@ thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
     v4f acc[MR];
 #pragma unroll
     for (int m = 0; m < MR; m++) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    if (n0 < N) {
-        const float* bp = B + (int64_t)k0 * ldb + n0;
+    if (col(0) < N) {
+        const float* bp = B + (int64_t)k0 * ldb;
         int k = k0;
         for (; k + kThinMUnroll <= k1; k += kThinMUnroll) {
             v4f b[kThinMUnroll];
 #pragma unroll
-            for (int u = 0; u < kThinMUnroll; u++)
-                b[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(bp + (int64_t)u * ldb));
+            for (int u = 0; u < kThinMUnroll; u++) b[u] = load_row(bp + (int64_t)u * ldb);
 #pragma unroll
             for (int u = 0; u < kThinMUnroll; u++)
 #pragma unroll
@@ -86,7 +102,7 @@ thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
             bp += (int64_t)kThinMUnroll * ldb;
         }
         for (; k < k1; k++, bp += ldb) {
-            const v4f b = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(bp));
+            const v4f b = load_row(bp);
 #pragma unroll
             for (int m = 0; m < MR; m++) {
                 const float a = TA ? A[(int64_t)k * lda + m] : A[(int64_t)m * lda + k];
@@ -101,23 +117,41 @@ thin_m(int N, int K, int kchunk, const float* __restrict__ A, int64_t lda,
         for (int m = 0; m < MR; m++) red[w - 1][lane][m] = acc[m];
     }
     __syncthreads();
-    if (w > 0 || n0 >= N) return;
+    if (w > 0 || col(0) >= N) return;
 #pragma unroll
     for (int v = 0; v < 3; v++)
 #pragma unroll
         for (int m = 0; m < MR; m++) acc[m] += red[v][lane][m];
     if (slab) {
-        float* o = out + (int64_t)z * slab + n0;
+        float* o = out + (int64_t)z * slab;
 #pragma unroll
-        for (int m = 0; m < MR; m++) *reinterpret_cast<v4f*>(o + (int64_t)m * ldo) = acc[m];
+        for (int m = 0; m < MR; m++) {
+            if constexpr (VB) {
+                *reinterpret_cast<v4f*>(o + (int64_t)m * ldo + col(0)) = acc[m];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if (col(e) < N) o[(int64_t)m * ldo + col(e)] = acc[m][e];
+            }
+        }
     } else {
 #pragma unroll
         for (int m = 0; m < MR; m++) {
-            const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
-            if (tc)
-                store_c(out + (int64_t)n0 * ldo + m, ldo, v, 4, alpha, beta);
-            else
-                store_c(out + (int64_t)m * ldo + n0, 1, v, 4, alpha, beta);
+            if constexpr (VB) {
+                const float v[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+                if (tc)
+                    store_c(out + (int64_t)col(0) * ldo + m, ldo, v, 4, alpha, beta);
+                else
+                    store_c(out + (int64_t)m * ldo + col(0), 1, v, 4, alpha, beta);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if (col(e) >= N) break;
+                    const float v = acc[m][e];
+                    store_c(tc ? out + (int64_t)col(e) * ldo + m : out + (int64_t)m * ldo + col(e), 1, &v, 1,
+                            alpha, beta);
+                }
+            }
         }
     }
 }
@@ -245,11 +279,18 @@ hipError_t launch_thin_m_r(const GemmArgs& g, int splits, int kchunk, float* ws,
     const dim3 grid((unsigned)ceil_div(g.N, 256), (unsigned)splits);
     float* out = splits > 1 ? ws : g.C;
     const int64_t ldo = splits > 1 ? g.N : g.ldc, slab = splits > 1 ? g.M * g.N : 0;
-    if (g.trans_a)
-        hipLaunchKernelGGL((thin_m<MR, true>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
+    const bool vb = rows_vec(g.B, g.ldb, g.N);
+    if (g.trans_a && vb)
+        hipLaunchKernelGGL((thin_m<MR, true, true>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
+    else if (vb)
+        hipLaunchKernelGGL((thin_m<MR, false, true>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
+                           kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
+    else if (g.trans_a)
+        hipLaunchKernelGGL((thin_m<MR, true, false>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
                            kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
     else
-        hipLaunchKernelGGL((thin_m<MR, false>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
+        hipLaunchKernelGGL((thin_m<MR, false, false>), grid, dim3(kThinThreads), 0, s, (int)g.N, (int)g.K,
                            kchunk, g.A, g.lda, g.B, g.ldb, out, ldo, slab, g.alpha, g.beta, tc);
     return hipGetLastError();
 }

@@ -356,9 +356,9 @@ def test_plan_config_thin(lib):
     assert c["engine"] == "thin" and c["tile"] == (8, 32)
     assert cfg(1, 16384, 16384, transb=True, ldb=16384)["tile"] == (1, 16)
     assert cfg(1, 8192, 8192, transb=True, ldb=8192)["engine"] == "mfma"   # from 384 MB when transposed
-    assert cfg(16384, 8, 16384, transa=True, lda=16385)["engine"] == "mfma"  # rows not 16-byte chunks
+    assert cfg(16384, 8, 16384, transa=True, lda=16385)["engine"] == "thin"  # rows not 16-byte chunks: 4-byte loads
     assert cfg(16, 16384, 16384)["engine"] == "mfma"              # not thin
-    assert cfg(1, 16383, 16384)["engine"] == "mfma"               # B rows not 16-byte chunks
+    assert cfg(1, 16383, 16384)["engine"] == "thin"               # B rows not 16-byte chunks: 4-byte loads
     assert cfg(16384, 1, 16383)["engine"] == "thin"               # A rows not 16-byte chunks: 4-byte loads
     assert cfg(1 << 27, 1, 4)["engine"] == "thin"                 # rows the thin_n grid can count
     assert cfg((1 << 27) + 4, 1, 4)["engine"] == "mfma"
