@@ -166,9 +166,9 @@ int sgemm_split_plan(int transa, int transb, int64_t M, int64_t N, int64_t K,
  * these operands: host-only, no HIP call; the pointers enter only through
  * their alignment.  Writes the engine (*engine: 1 = the matrix-core kernel,
  * 2 = the thin-product kernels on the vector units, for M <= 8 or N <= 8
- * when the large operand suits 16-byte loads and is 384 MB or more, 256 MB
- * or more for 2 <= N <= 4, or 16 MB or more for N == 1; stored with K
- * contiguous on the other side, 384 MB or more), the
+ * when the large operand is 384 MB or more, 256 MB or more for 2 <= N <= 4,
+ * or 16 MB or more for N == 1; stored with K contiguous on the other side,
+ * 384 MB or more), the
  * workgroup's C tile (*tile_m x *tile_n), the number of K ranges one
  * workgroup splits its work into (*k_groups), whether the operands are
  * first copied into zero-padded aligned rows (*packed, 1 or 0) and the K
