@@ -306,11 +306,19 @@ static ThinPlan thin_plan_direct(const GemmArgs& g, bool transposed) {
     // original keeps 16-byte loads there (1 x 8192 x 8192 with B stored N x K:
     // 48.7 us on the matrix cores, 50.0 on thin_n).
     const int64_t min_n = transposed ? kMinBytes : g.N == 1 ? kMinColumn : g.N <= 4 ? kMinFewColumns : kMinBytes;
-    if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= kMinBytes) {
+    // A streamed operand whose rows are not whole 16-byte chunks leaves the
+    // matrix cores their 4-byte path, which the thin kernels beat from
+    // 16 MB for up to 4 rows or columns of C (us: 1 x 8191 x 8192 76 -> 60,
+    // 8192 x 4 x 8191 76 -> 52, 8192 x 3 x 4095 41.8 -> 27.9, 1 x 4095 x 4096
+    // 25.5 -> 21.1) but not for 8 (8 x 4095 x 4096 25.7 -> 27.7).
+    const bool few_m = g.M <= 4 && !rows_vec(g.B, g.ldb, g.N);
+    const bool few_n = g.N <= 4 && !rows_vec(g.A, g.lda, g.K);
+    if (g.M <= 8 && !g.trans_b && 4 * g.K * g.N >= (few_m ? kMinColumn : kMinBytes)) {
         t.kind = ThinPlan::THIN_M;
         groups = ceil_div(g.N, 256);
         min_chunk = 256;
-    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= min_n && g.M <= kMaxThinRows) {
+    } else if (g.N <= 8 && !g.trans_a && 4 * g.M * g.K >= (few_n ? kMinColumn : min_n) &&
+               g.M <= kMaxThinRows) {
         t.kind = ThinPlan::THIN_N;
         t.waves = g.N <= 2 && g.M >= 16384 ? 4 : 8;
         groups = ceil_div(g.M, 4 * t.waves);

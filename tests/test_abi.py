@@ -360,6 +360,9 @@ def test_plan_config_thin(lib):
     assert cfg(16, 16384, 16384)["engine"] == "mfma"              # not thin
     assert cfg(1, 16383, 16384)["engine"] == "thin"               # B rows not 16-byte chunks: 4-byte loads
     assert cfg(16384, 1, 16383)["engine"] == "thin"               # A rows not 16-byte chunks: 4-byte loads
+    # Unaligned streams with up to 4 rows or columns of C: from 16 MB.
+    assert cfg(1, 4095, 4096)["engine"] == "thin" and cfg(4096, 3, 2047)["engine"] == "thin"
+    assert cfg(8, 4095, 4096)["engine"] == "mfma" and cfg(8192, 8, 8191)["engine"] == "mfma"
     assert cfg(1 << 27, 1, 4)["engine"] == "thin"                 # rows the thin_n grid can count
     assert cfg((1 << 27) + 4, 1, 4)["engine"] == "mfma"
     # A split request bypasses the thin path.

@@ -77,9 +77,11 @@ THIN_N = [(0, 0, 4096, 1, 1024), (0, 0, 4100, 1, 1028), (0, 1, 16385, 2, 6144), 
 THIN_T = [(0, 1, 1, 24576, 4096), (1, 1, 5, 16388, 6148), (1, 0, 98308, 1, 1028), (1, 0, 16392, 2, 8192),
           (1, 1, 12292, 7, 8200), (0, 1, 1, 24576, 4097)]
 # The streamed operand's rows not in 16-byte chunks (K or N odd): thin_n and
-# thin_m with 4-byte loads, direct and transposed.
+# thin_m with 4-byte loads, direct and transposed; from 16 MB for up to 4
+# rows or columns of C.
 THIN_U = [(0, 0, 16384, 1, 16383), (0, 1, 12289, 3, 8191), (0, 0, 100003, 4, 1023), (0, 0, 1, 16383, 16384),
-          (1, 0, 3, 24575, 4097), (1, 0, 16383, 1, 16384), (0, 0, 2, 65535, 4096)]
+          (1, 0, 3, 24575, 4097), (1, 0, 16383, 1, 16384), (0, 0, 2, 65535, 4096), (0, 0, 1, 4095, 4096),
+          (0, 0, 4096, 3, 2047)]
 
 
 @pytest.mark.parametrize("case", THIN_M + THIN_N + THIN_T + THIN_U, ids=lambda c: "{}{}-{}x{}x{}".format(*c))
