@@ -6,26 +6,26 @@
 // Bandwidths and peak rate - exercises", exercises 4 and 6: a kernel's
 // intensity against the ridge decides which roof applies), and a 32 x 32
 // matrix-core tile would mostly multiply padding.  These kernels stream the
-// large operand in 16-byte loads along its contiguous dimension, one pass,
-// and keep the small one close:
-//  * thin_m (M <= 8, B stored K x N): lane owns 4 columns of C; a wave's
-//    loads of one row of B are 1 KB contiguous (four 256-byte runs of 4-byte
-//    loads when B's rows are not whole 16-byte chunks); the M values of A a step
+// large operand along its contiguous dimension, one pass, in 16-byte loads
+// (4-byte ones, each wave instruction still 256 contiguous bytes, when its
+// rows are not whole 16-byte chunks), and keep the small one close:
+//  * thin_m (M <= 8, B stored K x N): lane owns 4 columns of C, so a wave's
+//    loads of one row of B are 1 KB contiguous; the M values of A a step
 //    needs are the same for every lane (scalar loads).  The workgroup's four
 //    waves take four consecutive K ranges of the chunk and add their partial
 //    columns in wave order through LDS.
 //  * thin_n (N <= 8, A stored M x K): a wave owns 4 rows of C and its lanes
-//    split K, 4 consecutive k per lane per step (or 4 k 64 apart, with
-//    4-byte loads, when A's rows are not whole 16-byte chunks), UN steps'
-//    loads in flight;
-//    the workgroup (WAVES waves: 8 with UN 2, or 4 with UN 1 for long A of
-//    one or two columns) stages B (K x N or N x K) through LDS, k-major per
-//    column, in pieces of 1024 k.  Lane partial sums are added by a fixed
-//    butterfly across the wave.
+//    split K, 4 k per lane per step, UN steps' loads in flight; the
+//    workgroup (WAVES waves: 8 with UN 2, or 4 with UN 1 for long A of one or
+//    two columns) stages B (K x N or N x K) through LDS, k-major per column,
+//    in pieces of 1024 k.  Lane partial sums are added by a fixed butterfly
+//    across the wave.
 // Both take a K chunk per gridDim.y: with one chunk they write C
 // (alpha * sum, then fmaf(beta, C, .) when beta != 0, as every other path);
-// with several they write dense partial slabs that splitk_reduce adds in
-// chunk order.  Every order is fixed, so a call is bit-reproducible.
+// with several they write dense partial slabs that a reduction adds in
+// chunk order.  Every order is fixed, so a call is bit-reproducible.  With
+// tc they store C transposed: the plan runs a product whose large operand
+// is stored with K contiguous on the other side as its transpose.
 #include <algorithm>
 
 #include "kernels.h"
