@@ -464,8 +464,10 @@ hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float
 
 // The four storage orientations of (A, B) for one tile configuration; with
 // splits > 1 (and CAN_SPLIT) the split-K pair of launches.
+// OCC_TN: the occupancy target for A stored K x M with B stored K x N,
+// whose index math needs more registers in some configurations.
 template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2,
-          int WK = 1, bool CAN_SPLIT = true>
+          int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,
                             float* ws = nullptr) {
     using k4::Cfg;
@@ -476,7 +478,7 @@ hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, in
             if (!g.trans_a && g.trans_b)
                 return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
             if (g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC_TN, SPLIT, WK>(g, splits, kchunk, ws, s);
             return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT, WK>(g, splits, kchunk, ws, s);
         }
     }
@@ -485,7 +487,7 @@ hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, in
     if (!g.trans_a && g.trans_b)
         return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT, WK>(g, s);
     if (g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC, SPLIT, WK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC_TN, SPLIT, WK>(g, s);
     return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT, WK>(g, s);
 }
 
@@ -546,7 +548,9 @@ hipError_t launch_k4_tile64(const GemmArgs& g, hipStream_t s) { return launch_k4
 
 hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
                                     float* ws) {
-    // Occupancy targets as the LDS allows them (2 and 4 workgroups per CU).
+    // Occupancy targets as the LDS allows them (3, 2 and 4 workgroups per
+    // CU; a target of 2 for the three-stage slabs of 16 held 768 x 1024 x
+    // 1024, 768 tiles, at 21.3 us against 18.7 with 3).
     // With 16-byte loads, K slabs of 16 in three stages (two slabs in
     // flight) when a K group's share is short or two workgroups share each
     // CU: 3-11 % faster than slabs of 32 in two stages on 17 such outputs
@@ -558,7 +562,7 @@ hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int k
         const int64_t share = (splits > 1 ? kchunk : g.K) / 4;
         const int64_t wgs = ceil_div(g.M, 32) * ceil_div(g.N, 32) * (splits > 1 ? splits : 1);
         if (share <= 256 || wgs >= 2 * 256)
-            return launch_k4_orient<1, 1, 1, 1, 16, true, 2, true, 3, 4>(g, s, splits, kchunk, ws);
+            return launch_k4_orient<1, 1, 1, 1, 16, true, 3, true, 3, 4, true, 2>(g, s, splits, kchunk, ws);
         return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4>(g, s, splits, kchunk, ws);
     }
     return launch_k4_orient<1, 1, 1, 1, 16, false, 4, false, 2, 4>(g, s, splits, kchunk, ws);
