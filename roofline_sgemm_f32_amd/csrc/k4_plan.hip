@@ -33,13 +33,16 @@ namespace sgemm {
 //    against 13.2), and with 4-byte loads below 512 tiles of 64 x 64 as well
 //    (1024 x 1027 x 1024: 41.5 against 52.0).  A wave's chain of dependent
 //    matrix instructions is what bounds these shapes: 32 x 32 tiles give more
-//    workgroups, K groups shorten each chain.  With K <= 1024 also up to 768
+//    workgroups, K groups shorten each chain.  With K <= 2048 also up to 768
 //    tiles, unsplit (three workgroups per CU, one round), in place of 64 x 64
-//    tiles with K groups or a split of 2 (640^3 16.3 us -> 10.3, 704^3 17.5
-//    -> 11.0, 512 x 1024 x 1024 17.7 -> 14.3, 768^3 18.6 -> 17.1, 800^3
-//    19.7 -> 18.1); with 784 or more tiles (896^3 21.3 -> 24.0, 1024^3 23.7
-//    -> 26.6) or longer K (640^2 x 2048 25.9 -> 30.0, 768^2 x 2048 32.6 ->
-//    40.8) the 64 x 64 choice stays.
+//    tiles with K groups or a split (640^3 16.3 us -> 10.3, 704^3 17.5 ->
+//    11.0, 512 x 1024 x 1024 17.7 -> 14.3, 768 x 1024 x 1280 28.1 -> 22.6,
+//    1024 x 768 x 2048 35.5 -> 33.5, 640^2 x 1536 21.9 -> 20.5; 640^2 x 2048
+//    25.8 -> 26.1 and 768^2 x 2048 32.6 -> 33.3 the exceptions); on packed
+//    copies only up to K = 1024 (800 x 801 x 2047 41.5 us split on 64 x 64
+//    tiles against 43.8); with 784 or more tiles (896^3 21.3 -> 24.0, 1024^3
+//    23.7 -> 26.6) or longer K (512 x 768 x 4096 35.9 -> 44.3) the 64 x 64
+//    choice stays.
 //  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
 //    SIMD, fragments read in halves, raised wave priority during the
 //    matrix instructions) when the tiles fill whole rounds of 2 per CU, or
@@ -133,7 +136,7 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     } else if (T64 >= 512 || (vec && T64 > 256 && T32 > 256)) {
         cfg = K4_T64;
         tiles = T64;
-    } else if (T32 <= 256 || !vec || (T32 <= 3 * kCUs && g.K <= 1024)) {
+    } else if (T32 <= 256 || !vec || (T32 <= 3 * kCUs && g.K <= (g.runs_padded ? 1024 : 2048))) {
         cfg = K4_T32_WK4;
         tiles = T32;
     } else {

@@ -252,12 +252,13 @@ def test_split_plan_choices(lib):
     assert plan(64, 16384, 4096) == 1
     # No chunk below 512 of K from the model.
     assert plan(768, 768, 768) == 1
-    for M, N, K in [(64, 8192, 2048), (768, 768, 4096), (512, 1024, 8192)]:
+    for M, N, K in [(64, 8192, 4096), (768, 768, 4096), (512, 1024, 8192)]:
         S, kc = rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED)
         assert S > 1 and kc >= 512 and kc % 32 == 0 and (S - 1) * kc < K <= S * kc
-    # Up to 768 tiles of 32 x 32 with K <= 1024 run unsplit on 32 x 32 tiles
+    # Up to 768 tiles of 32 x 32 with K <= 2048 run unsplit on 32 x 32 tiles
     # with K groups (one round of three workgroups per CU).
-    for M, N, K in [(64, 8192, 1024), (640, 640, 640), (512, 1024, 1024), (192, 4096, 1024)]:
+    for M, N, K in [(64, 8192, 1024), (640, 640, 640), (512, 1024, 1024), (192, 4096, 1024), (64, 8192, 2048),
+                    (768, 1024, 1280)]:
         assert rs.split_plan(M, N, K, A_ptr=ALIGNED, B_ptr=ALIGNED) == (1, K)
 
 
@@ -275,11 +276,11 @@ def test_plan_config_choices(lib):
     assert cfg(1024, 1024, 1024)["tile"] == (64, 64) and cfg(1024, 1024, 1024)["k_groups"] == 4
     small = cfg(256, 256, 256)
     assert small["tile"] == (32, 32) and small["k_groups"] == 4 and small["splits"] == 1
-    # Up to 768 such tiles with K <= 1024: one round of three workgroups per CU.
+    # Up to 768 such tiles with K <= 2048: one round of three workgroups per CU.
     mid = cfg(640, 640, 640)
     assert mid["tile"] == (32, 32) and mid["k_groups"] == 4 and mid["splits"] == 1
     assert cfg(896, 896, 896)["tile"] == (64, 64)     # 784 tiles of 32 x 32
-    assert cfg(640, 640, 2048)["tile"] == (64, 64)    # a longer K
+    assert cfg(640, 640, 4096)["tile"] == (64, 64)    # a longer K
     assert cfg(128, 128, 4096)["splits"] == 16
     skinny = cfg(64, 8192, 8192)
     assert skinny["tile"] == (64, 64) and skinny["k_groups"] == 1 and skinny["splits"] == 8
