@@ -350,6 +350,7 @@ SMALL_SHAPES = {
     "skinny64x8192x8192": (64, 8192, 8192),
     "thin1x16384x16384": (1, 16384, 16384),
     "column16384x1x16384": (16384, 1, 16384),
+    "mid768x1024x1024": (768, 1024, 1024),
 }
 
 
