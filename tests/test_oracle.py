@@ -65,18 +65,6 @@ def test_checker_accepts_float_rounding_and_rejects_errors():
     assert not r["ok"] and r["n_nonfinite"] == 1
 
 
-def test_checker_k_zero_requires_exact_zero():
-    z = np.zeros((2, 2))
-    assert check.check(np.zeros((2, 2), np.float32), z, z, 0)["ok"]
-    assert not check.check(np.full((2, 2), 1e-30, np.float32), z, z, 0)["ok"]
-
-
-def test_checker_page_relative_error_formula():
-    # max |g - r| / max(|r|, 1e-6), the figure the course's checker prints.
-    r = check.check(np.array([1.5, 0.0], np.float32), np.array([1.0, 0.0]), np.array([10.0, 1.0]), 1 << 20)
-    assert r["max_rel_err_page"] == pytest.approx(0.5)
-
-
 # --- mutation: each plausible mistake in the oracle must trip a pin ---------
 
 MUTANTS = {
