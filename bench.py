@@ -11,14 +11,21 @@ timed launches bracketed by events on the launch stream, mean per launch.
 Prints ONE JSON line on stdout; the ladder table and the copy-probe sweep
 (--ladder, --copy-sweep) go to stderr and to --out as JSON lines.
 
-Legs:
-  * GPU product: value = 2 M N K / mean step time.
+Legs, in the order they run:
+  * hbm_copy: the copy probe (256 Mi floats, 2 GiB moved) against 8 TB/s,
+    and compute_probe: register-only FMA chains and back-to-back FP32 matrix
+    instructions, the two roofs the kernels are measured against.
+  * GPU product (the headline): value = 2 M N K / mean step time.
   * roofline: the matrix-core kernel's achieved TFLOP/s against 157.3, from
-    per-launch events on the launch stream; ``traffic`` is read from a
-    committed counter summary when it was taken on the current kernel source.
-  * hbm_copy: the copy probe (256 Mi floats, 2 GiB moved) against 8 TB/s.
+    the events around the timed launches on the launch stream; ``traffic``
+    is read from a committed counter summary when it was taken on the
+    current kernel source.
+  * configs: each of the five workloads through AUTO (time per call,
+    GFLOP/s, fraction of the FP32 peak).
+  * small_shapes: the small-shape path, split as chosen and unsplit.
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
-    rows of the same product; its rows also gate the GPU result.
+    the headline product; the oracle's full results then gate every element
+    of the headline product and of each config's result.
 """
 from __future__ import annotations
 
@@ -151,9 +158,10 @@ def device_operands(w):
     return A_h, B_h, A, B, C
 
 
-def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float, threads: int | None = None):
+def cpu_baseline_leg(w, A_h, B_h, C, budget_s: float, threads: int | None = None):
     """Time the CPU oracle on a bounded sample of rows of the same product,
-    and check the GPU's rows against it."""
+    and check the GPU's rows against it (C: the GPU result, a host array or
+    a device tensor)."""
     import numpy as np
     import oracle
     from oracle import check
@@ -186,7 +194,8 @@ def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float, threads: int | None = 
     # Gate: the GPU rows against the oracle rows, with the bound matrix
     # (untimed).
     _, S = oracle.sgemm_rows_f64(An, Bn, rows, bound=True, threads=threads)
-    rep = check.check(C_dev[rows.tolist()].cpu().numpy(), ref, S, w.K)
+    Cr = C[rows] if isinstance(C, np.ndarray) else C[rows.tolist()].cpu().numpy()
+    rep = check.check(Cr, ref, S, w.K)
     base = {
         "value": round(m.gflops(flops, dt * 1e3), 3),
         "unit": "GFLOP/s",
@@ -209,6 +218,55 @@ def cpu_baseline_leg(w, A_h, B_h, C_dev, budget_s: float, threads: int | None = 
     gate = {"rows_checked": len(rows), "ok": rep["ok"], "max_bound_util": rep["max_bound_util"],
             "max_rel_err_page": rep["max_rel_err_page"], "n_violations": rep["n_violations"]}
     return base, gate
+
+
+def oracle_gate(w, A_h, B_h, C_host):
+    """Every element of a GPU result against the CPU oracle's bound (part
+    of the CPU leg: the oracle runs on this host's threads, untimed here)."""
+    import oracle
+    from oracle import check
+    from roofline_sgemm_f32_amd.inputs import as_numpy
+    ref, S = oracle.sgemm_f64(as_numpy(A_h), as_numpy(B_h))
+    rep = check.check(C_host, ref, S, w.K)
+    return {"elements_checked": rep["n"], "ok": rep["ok"], "max_bound_util": rep["max_bound_util"],
+            "max_rel_err_page": rep["max_rel_err_page"], "n_violations": rep["n_violations"]}
+
+
+def configs_leg(budget_s: float):
+    """The five workloads through AUTO: back-to-back calls for about
+    ``budget_s`` (at least 20, after as many warm-ups), mean per call.
+    Returns the records and, per workload, the host operands and the host
+    copy of the timed launches' result for the CPU leg's gate."""
+    import torch
+    import roofline_sgemm_f32_amd as rs
+    from roofline_sgemm_f32_amd import metrics as m
+    from roofline_sgemm_f32_amd.inputs import WORKLOADS
+    rows, keep = [], {}
+    for name, w in WORKLOADS.items():
+        A_h, B_h, A, B, C = device_operands(w)
+        fn = run_gemm_factory("auto", A, B, C)
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        steps = int(max(20, min(2000, budget_s / max(time.perf_counter() - t0, 1e-6))))
+        ms, _ = time_launches(fn, steps, steps, per_launch=False)
+        plan = rs.plan_config(w.M, w.N, w.K, lda=w.lda, ldb=w.ldb, A_ptr=A.data_ptr(),
+                              B_ptr=B.data_ptr())
+        g = m.gflops(m.sgemm_flops(w.M, w.N, w.K), ms)
+        rec = {"workload": name, "M": w.M, "N": w.N, "K": w.K, "dist": w.dist, "seed": w.seed,
+               "variant": "auto", "engine": plan["engine"], "tile": list(plan["tile"]),
+               "k_groups": plan["k_groups"], "packed": plan["packed"], "chunks": plan["splits"],
+               "ms": round(ms, 5), "gflops": round(g, 1),
+               "pct_peak": round(m.pct_of_peak(g, m.MI355X_FP32_PEAK_GFLOPS), 2), "steps": steps}
+        rows.append(rec)
+        keep[name] = (w, A_h, B_h, C.cpu().numpy())
+        log(f"  config {name:22s} {ms:9.4f} ms {g:10.1f} GFLOP/s {rec['pct_peak']:6.2f}% "
+            f"tile {plan['tile']} x{plan['k_groups']} packed={plan['packed']} chunks={plan['splits']}")
+        del A, B, C
+        torch.cuda.empty_cache()
+    return rows, keep
 
 
 def copy_probe(steps: int, block=None, grid=None):
@@ -486,6 +544,8 @@ def main():
                    help="comma-separated small shapes: time only these and print their JSON")
     p.add_argument("--cpu-all", action="store_true",
                    help="only: every workload on the GPU beside the CPU oracle (one JSON line each)")
+    p.add_argument("--configs-seconds", type=float, default=0.2,
+                   help="timed calls per workload in the configs section (0 skips it)")
     args = p.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -511,6 +571,20 @@ def main():
                                                        args.small_only.split(","))}), flush=True)
         return
 
+    # The roofs first: the copy probe and the compute probes calibrate the
+    # denominators the kernels are measured against.  (They also leave the
+    # GPU clock up: on a cold GPU the first ~0.1 s of launches run up to
+    # 25 % slower while the clock rises.)
+    copy = copy_probe(args.copy_steps) if args.copy_steps > 0 else None
+    if copy:
+        log(f"[bench] copy probe {copy['gbs']} GB/s ({100 * copy['frac']:.1f}% of 8 TB/s)")
+    probe = compute_probe() if args.compute_probe else None
+    if probe:
+        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s "
+            f"(best {probe['valu_fma_tflops_best']}), FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s "
+            f"(best {probe['mfma_f32_tflops_best']})")
+    torch.cuda.empty_cache()
+
     w = WORKLOADS[args.workload]
     A_h, B_h, A, B, C = device_operands(w)
     variant = args.variant
@@ -531,15 +605,11 @@ def main():
     peak_tf = m.MI355X_FP32_PEAK_GFLOPS / 1e3
     log(f"[bench] {ms_step:.4f} ms/step, {value:.1f} GFLOP/s, "
         f"{m.pct_of_peak(value, m.MI355X_FP32_PEAK_GFLOPS):.2f}% of FP32 peak")
+    # The timed launches' result, checked by the CPU leg.
+    C_host = C.cpu().numpy()
+    del A, B, C
+    torch.cuda.empty_cache()
 
-    copy = copy_probe(args.copy_steps) if args.copy_steps > 0 else None
-    if copy:
-        log(f"[bench] copy probe {copy['gbs']} GB/s ({100 * copy['frac']:.1f}% of 8 TB/s)")
-    probe = compute_probe() if args.compute_probe else None
-    if probe:
-        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s "
-            f"(best {probe['valu_fma_tflops_best']}), FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s "
-            f"(best {probe['mfma_f32_tflops_best']})")
     if args.copy_sweep:
         from roofline_sgemm_f32_amd.inputs import COPY_ELEMENTS  # noqa: F401
         for block in (64, 128, 256, 512, 1024):
@@ -550,16 +620,24 @@ def main():
                     out.write(json.dumps({"copy_sweep": r}) + "\n")
     if args.ladder:
         ladder(args, out)
+    configs, keep = (configs_leg(args.configs_seconds) if args.configs_seconds > 0 else (None, {}))
     small = small_shapes(args.small_reps) if args.small_reps > 0 else None
 
     # The CPU leg runs last: the GPU clock falls during its seconds of GPU
-    # idleness, which would slow the probes timed after it.  C still holds
-    # the timed product, which the leg checks.
+    # idleness, which would slow GPU work timed after it.  The oracle's
+    # results gate the headline product and every config's.
     cpu, gate = None, None
     if args.cpu_seconds > 0:
-        log(f"[bench] cpu baseline leg (~{args.cpu_seconds:.0f} s)")
-        cpu, gate = cpu_baseline_leg(w, A_h, B_h, C, args.cpu_seconds)
+        log(f"[bench] cpu baseline leg (~{args.cpu_seconds:.0f} s, then the full-product gates)")
+        cpu, gate = cpu_baseline_leg(w, A_h, B_h, C_host, args.cpu_seconds)
         log(f"[bench] oracle {cpu['value']} GFLOP/s; gate {gate}")
+        for rec in configs or []:
+            cw, ca, cb, cc = keep[rec["workload"]]
+            rec["gate"] = oracle_gate(cw, ca, cb, cc)
+            if not rec["gate"]["ok"]:
+                rec["gflops"] = rec["pct_peak"] = None
+            log(f"  gate {rec['workload']:22s} {rec['gate']}")
+        keep.clear()
 
     traffic = read_traffic(resolved, w.name)
     kernel = resolved
@@ -588,6 +666,7 @@ def main():
         "gate": gate,
         "hbm_copy": copy,
         "compute_probe": probe,
+        "configs": configs,
         "small_shapes": small,
     }
     if out:
@@ -595,6 +674,8 @@ def main():
         out.close()
     print(json.dumps(line), flush=True)
     if gate is not None and not gate["ok"]:
+        sys.exit(3)
+    if any(not r.get("gate", {"ok": True})["ok"] for r in configs or []):
         sys.exit(3)
 
 

@@ -21,13 +21,40 @@
  *   (C).  Pointers need only 4-byte alignment; 16-byte alignment with lda,
  *   ldb, K and N multiples of 4 selects wider loads internally.
  *
- * Ownership and concurrency
+ * Ownership, memory and synchronisation (per entry point)
  *   A, B and C are device pointers owned by the caller (for example the data
- *   of torch tensors).  The library allocates no device memory, keeps no
- *   per-call state and is reentrant.  The work is enqueued on ``stream``
- *   (a hipStream_t; NULL means the null stream) and the call returns without
- *   synchronising; a device fault surfaces at the caller's next
- *   synchronisation.
+ *   of torch tensors); the library never frees or keeps them.  Every entry
+ *   point enqueues its work on ``stream`` (a hipStream_t; NULL means the null
+ *   stream) and returns without waiting for that work; a device fault
+ *   surfaces at the caller's next synchronisation.
+ *
+ *   The caller-owns-everything reading of the course's scaffolding (the
+ *   harness allocates every buffer) holds for sgemm_f32_variant with the
+ *   ladder variants 1-3, 5-8 and 9-11 and for the copy and compute probes:
+ *   they allocate no device memory and never synchronise.  The shape-chosen paths depart from it in one place, a
+ *   library workspace:
+ *     - sgemm_f32 and SGEMM_AUTO, SGEMM_K4_MFMA, sgemm_f32_ex,
+ *       sgemm_f32_colmajor and sgemm_f32_ex_split use scratch device memory
+ *       when their plan (sgemm_plan_config) splits K across workgroups
+ *       (partial products), packs unaligned operands into zero-padded
+ *       aligned copies first (for example the 3001 x 4099 x 2047 product,
+ *       whose packed copies take about 58 MB), or splits a thin product's K;
+ *     - that scratch is one buffer per device, allocated stream-ordered from
+ *       a memory pool the library creates, on first need, grown on demand
+ *       up to 256 MiB and kept until the process ends; a larger request gets
+ *       a buffer of its own, freed stream-ordered after its call;
+ *     - calls that use it on one device take it in turn (a host lock around
+ *       their launches).  While every such call has used one stream, the
+ *       stream alone orders them.  The first such call on a second stream
+ *       synchronises the whole device once (hipDeviceSynchronize: it must
+ *       not coincide with a graph capture on another thread); from then on
+ *       a call on another stream than the previous one waits for it on the
+ *       GPU through an event;
+ *     - if the workspace cannot be allocated, the same product runs without
+ *       it (unsplit, unpacked), and so do calls made while ``stream`` is
+ *       being captured into a graph.
+ *   Every other case of these entry points (products that neither split nor
+ *   pack, K == 0, alpha == 0) allocates nothing and never synchronises.
  *
  * Errors
  *   Arguments are validated on the host before any HIP call; a bad argument
@@ -46,25 +73,42 @@ extern "C" {
 #endif
 
 /* Kernel ladder.  Every variant computes the same product and accepts every
- * shape the validation above accepts (SGEMM_K4_MFMA excepted, see
- * SGEMM_ERR_UNSUPPORTED); they differ in how they use the chip.  Variants
- * 0-4 are the ladder proper; 5-10 are comparison points. */
+ * shape the validation above accepts (the SGEMM_K4_MFMA variants excepted,
+ * see SGEMM_ERR_UNSUPPORTED); they differ in how they use the chip.  Stages
+ * are those of amittech.dev, "3.5 Project: tiled matrix multiplication",
+ * section "what we build - the GEMM ladder".  Variants 0-4 are the ladder
+ * proper; 5-11 are comparison points. */
 typedef enum sgemm_variant {
-    SGEMM_AUTO = 0,               /* pick per shape (the matrix-core kernel for large shapes) */
-    SGEMM_K1_COALESCED = 1,       /* one output per lane, lanes along a row of C (coalesced B/C, uniform A) */
-    SGEMM_K2_LDS_TILED = 2,       /* 32 x 32 LDS tiles of A and B per K step; one output per lane */
-    SGEMM_K3_REGTILE_DB = 3,      /* 128 x 128 workgroup tile, 8 x 8 outputs per lane in VGPRs, LDS double buffer */
-    SGEMM_K4_MFMA = 4,            /* FP32 matrix-core kernel (v_mfma_f32_32x32x2_f32), direct global->LDS
-                                     loads; 128 x 256, 128 x 128, 64 x 64 or 32 x 32 workgroup tiles, K
-                                     split and operand packing chosen by shape (sgemm_plan_config); thin
-                                     products (M or N <= 8, large operand) run on the vector units */
-    SGEMM_K2_LDS_TILED16 = 5,     /* as K2 with 16 x 16 tiles */
+    SGEMM_AUTO = 0,               /* pick per shape: the SGEMM_K4_MFMA path, or for products with
+                                     one side of C at most 8 and a large operand the thin-product
+                                     kernels on the vector units (sgemm_plan_config, engine 2);
+                                     the register-tiled kernel for shapes beyond the matrix-core
+                                     kernel's 32-bit offsets */
+    SGEMM_K1_COALESCED = 1,       /* section "stage 1 - global memory coalescing": one output per
+                                     lane, the 64 lanes of a wave along a row of C (coalesced B
+                                     and C, wave-uniform A) */
+    SGEMM_K2_LDS_TILED = 2,       /* section "stage 2 - shared memory tiling": 32 x 32 LDS tiles of
+                                     A and B per K step, one output per lane */
+    SGEMM_K3_REGTILE_DB = 3,      /* section "what comes next" (register tiling, double
+                                     buffering) and qsysarch.com "gemm-kernels", section
+                                     "improving the naive multiplier" (several outputs per
+                                     thread): 128 x 128 workgroup tile, 8 x 8 outputs per lane in
+                                     VGPRs, LDS double buffer */
+    SGEMM_K4_MFMA = 4,            /* section "what comes next" (the matrix units): FP32 matrix-core
+                                     kernel (v_mfma_f32_32x32x2_f32), direct global->LDS loads;
+                                     128 x 256, 128 x 128, 64 x 64 or 32 x 32 workgroup tiles, K
+                                     split and operand packing chosen by shape.  Always the
+                                     matrix cores (never the thin-product kernels of AUTO) */
+    SGEMM_K2_LDS_TILED16 = 5,     /* as K2 with 16 x 16 tiles (the section's TILE = 16 vs 32
+                                     comparison, "acceptance criteria") */
     SGEMM_K2_LDS_TILED_PAD1 = 6,  /* as K2 with rows padded by one float (LDS bank comparison) */
-    SGEMM_K0_NAIVE = 7,           /* one output per lane, lanes down a column of C (uncoalesced foil) */
+    SGEMM_K0_NAIVE = 7,           /* section "stage 0 - the naive baseline": one output per lane,
+                                     the lanes of a wave down a column of C (uncoalesced) */
     SGEMM_K2_LDS_TILED16_PAD1 = 8,/* as K2_LDS_TILED16 with rows padded by one float */
-    SGEMM_K4_MFMA_TILE128 = 9,    /* K4 with 128 x 128 tiles whatever the shape */
-    SGEMM_K4_MFMA_TILE64 = 10,    /* K4 with 64 x 64 tiles whatever the shape */
-    SGEMM_K4_MFMA_TILE128X256 = 11, /* K4 with 128 x 256 tiles whatever the shape */
+    SGEMM_K4_MFMA_TILE128 = 9,    /* K4 with 128 x 128 tiles whatever the shape, unsplit, unpacked */
+    SGEMM_K4_MFMA_TILE64 = 10,    /* K4 with 64 x 64 tiles whatever the shape, unsplit, unpacked */
+    SGEMM_K4_MFMA_TILE128X256 = 11, /* K4 with 128 x 256 tiles whatever the shape (128 x 128 for
+                                     transposed operands without 16-byte loads), unsplit */
     SGEMM_VARIANT_COUNT = 12
 } sgemm_variant_t;
 
@@ -123,20 +167,9 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
  * each stores its partial product to a workspace of chunks x M rows of N
  * floats (rows rounded up to a multiple of 4),
  * and a second kernel adds the partials in chunk order and applies alpha and
- * beta.  The workspace is library memory: one buffer per device, allocated
- * stream-ordered (from a memory pool the library creates) on first need,
- * grown on demand up to 256 MiB and kept for later calls; a larger request
- * gets a buffer of its own, freed stream-ordered after the call.  Split calls
- * on one device take the buffer in turn (a host lock around their launches).
- * While every call has used one stream, the stream alone orders them; the
- * first call on a second stream synchronizes the device once (as
- * hipDeviceSynchronize, so it must not coincide with a graph capture on
- * another thread), and from then on a call on another stream than the
- * previous one waits for it on the GPU through an event.
- * If the workspace cannot be allocated the product runs unsplit, and so do
- * calls made while `stream` is being captured into a graph (the workspace
- * paths, split-K and the packing of unaligned operands, are skipped there,
- * so that every entry point can be captured).
+ * beta.  The partial products live in the library workspace (see "Ownership,
+ * memory and synchronisation" above); a call made while `stream` is being
+ * captured into a graph runs unsplit and unpacked.
  *   splits == 0: chosen by shape (what sgemm_f32 and sgemm_f32_ex do);
  *   splits == 1: never split;
  *   2 <= splits <= SGEMM_MAX_SPLITS: at most that many chunks (fewer when K

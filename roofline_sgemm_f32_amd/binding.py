@@ -199,11 +199,13 @@ def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0, sp
     args = (int(transa), int(transb), M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(),
             _ld(B, "B"), beta, out.data_ptr(), _ld(out, "out"))
     if splits is None:
+        name = "sgemm_f32_ex"
         st = load().sgemm_f32_ex(*args, _stream_handle(A.device))
     else:
+        name = "sgemm_f32_ex_split"
         st = load().sgemm_f32_ex_split(*args, int(splits), _stream_handle(A.device))
     if st != 0:
-        raise SgemmError(st, "sgemm_f32_ex" if splits is None else "sgemm_f32_ex_split")
+        raise SgemmError(st, name)
     return out
 
 

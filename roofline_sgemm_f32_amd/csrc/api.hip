@@ -100,7 +100,12 @@ int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float*
     hipStream_t s = static_cast<hipStream_t>(stream);
     const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
     if (K == 0) return launch_status(sgemm::launch_zero(C, M, N, ldc, s));
-    if (variant == SGEMM_AUTO) variant = choose_auto(g);
+    if (variant == SGEMM_AUTO) {
+        // AUTO may also take the thin-product kernels (vector units) for
+        // products with one side of C at most 8.
+        if (choose_auto(g) == SGEMM_K4_MFMA) return launch_status(sgemm::launch_k4_mfma(g, s, 0, true));
+        return launch_status(sgemm::launch_k3_regtile(g, s));
+    }
     switch (variant) {
         case SGEMM_K0_NAIVE: return launch_status(sgemm::launch_k0_naive(g, s));
         case SGEMM_K1_COALESCED: return launch_status(sgemm::launch_k1_coalesced(g, s));
@@ -111,7 +116,8 @@ int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float*
         case SGEMM_K3_REGTILE_DB: return launch_status(sgemm::launch_k3_regtile(g, s));
         case SGEMM_K4_MFMA:
             if (!sgemm::k4_supports(g)) return SGEMM_ERR_UNSUPPORTED;
-            return launch_status(sgemm::launch_k4_mfma(g, s));
+            // Always the matrix cores (tile, K split and packing by shape).
+            return launch_status(sgemm::launch_k4_mfma(g, s, 0, false));
         case SGEMM_K4_MFMA_TILE128:
             if (!sgemm::k4_supports(g)) return SGEMM_ERR_UNSUPPORTED;
             return launch_status(sgemm::launch_k4_tile128(g, s));

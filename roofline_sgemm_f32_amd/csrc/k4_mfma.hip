@@ -109,6 +109,10 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     constexpr int LDS_TOTAL = CF::LDS_BYTES * WK > RED_BYTES ? CF::LDS_BYTES * WK : RED_BYTES;
     static_assert(WK >= 1 && WK <= 8 && CF::THREADS * WK <= 1024, "K groups");
     static_assert(LDS_TOTAL <= 160 * 1024, "LDS per workgroup");
+    // OCC waves per SIMD make OCC * 4 / (waves per workgroup) resident
+    // workgroups per CU, and their LDS must fit the CU's 160 KiB.
+    static_assert((OCC * 4 / (CF::NWAVES * WK)) * LDS_TOTAL <= 160 * 1024,
+                  "occupancy target exceeds the CU's LDS");
     if constexpr (SPLITK) {
         const int z = blockIdx.y, k0 = z * kchunk;
         K = K - k0 < kchunk ? K - k0 : kchunk;
@@ -464,8 +468,11 @@ hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float
 
 // The four storage orientations of (A, B) for one tile configuration; with
 // splits > 1 (and CAN_SPLIT) the split-K pair of launches.
-// OCC_TN: the occupancy target for A stored K x M with B stored K x N,
-// whose index math needs more registers in some configurations.
+// OCC_TN: the occupancy target for A stored K x M with B stored K x N.
+// Both operands then take the KRows layout, whose stages are larger: in the
+// three-stage 32 x 32 configuration with K slabs of 16 a workgroup needs
+// 55,296 B of LDS (52,224 B with A stored M x K), so three workgroups would
+// need 165,888 B, more than the CU's 160 KiB, and the target drops to 2.
 template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2,
           int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,

@@ -37,8 +37,11 @@ namespace sgemm {
 //    tiles, unsplit (three workgroups per CU, one round), in place of 64 x 64
 //    tiles with K groups or a split (640^3 16.3 us -> 10.3, 704^3 17.5 ->
 //    11.0, 512 x 1024 x 1024 17.7 -> 14.3, 768 x 1024 x 1280 28.1 -> 22.6,
-//    1024 x 768 x 2048 35.5 -> 33.5, 640^2 x 1536 21.9 -> 20.5; 640^2 x 2048
-//    25.8 -> 26.1 and 768^2 x 2048 32.6 -> 33.3 the exceptions); on packed
+//    1024 x 768 x 2048 35.5 -> 33.5, 640^2 x 1536 21.9 -> 20.5).  Two
+//    shapes measured 1-2 % slower under the rule (640^2 x 2048 25.8 ->
+//    26.1, 768^2 x 2048 32.6 -> 33.3); a carve-out for them would need a
+//    third bound on K x tiles that no other shape supports, and the rule's
+//    gains elsewhere are 5-20 %, so it keeps them.  On packed
 //    copies only up to K = 1024 (800 x 801 x 2047 41.5 us split on 64 x 64
 //    tiles against 43.8); with 784 or more tiles (896^3 21.3 -> 24.0, 1024^3
 //    23.7 -> 26.6) or longer K (512 x 768 x 4096 35.9 -> 44.3) the 64 x 64
@@ -244,19 +247,32 @@ static bool packing_plan(const GemmArgs& g, PackPlan* pk) {
     return true;
 }
 
-static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
+static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done,
+                                const FixedScratch* fixed) {
     *done = false;
     PackPlan pk;
     if (!packing_plan(g, &pk)) return hipSuccess;
     // Workspace: A's copy, B's copy, then the split's partial products,
     // each on a 256-byte boundary.
-    const size_t p_bytes = pk.p.splits > 1 ? size_t(pk.p.ws_floats) * sizeof(float) : 0;
+    size_t p_bytes = pk.p.splits > 1 ? size_t(pk.p.ws_floats) * sizeof(float) : 0;
     Workspace ws;
-    if (workspace_acquire(pk.a_bytes + pk.b_bytes + p_bytes, s, &ws) != hipSuccess) {
-        (void)hipGetLastError();
-        return hipSuccess;  // no workspace: the 4-byte path
+    char* base;
+    if (fixed) {
+        // A fixed scratch too small for the partial products runs the packed
+        // product unsplit; too small for the copies, the 4-byte path.
+        if (pk.a_bytes + pk.b_bytes + p_bytes > fixed->bytes) {
+            if (pk.a_bytes + pk.b_bytes > fixed->bytes) return hipSuccess;
+            pk.p.splits = 1;
+            p_bytes = 0;
+        }
+        base = reinterpret_cast<char*>(fixed->ptr);
+    } else {
+        if (workspace_acquire(pk.a_bytes + pk.b_bytes + p_bytes, s, &ws) != hipSuccess) {
+            (void)hipGetLastError();
+            return hipSuccess;  // no workspace: the 4-byte path
+        }
+        base = static_cast<char*>(ws.ptr);
     }
-    char* base = static_cast<char*>(ws.ptr);
     float* pa = reinterpret_cast<float*>(base);
     float* pb = reinterpret_cast<float*>(base + pk.a_bytes);
     float* pp = pk.p.splits > 1 ? reinterpret_cast<float*>(base + pk.a_bytes + pk.b_bytes) : nullptr;
@@ -272,8 +288,9 @@ static hipError_t launch_packed(const GemmArgs& g, hipStream_t s, bool* done) {
     if (pk.pack_a) gp.A = pa;
     if (pk.pack_b) gp.B = pb;
     if (e == hipSuccess) e = launch_plan(gp, pk.p, pp, s);
-    const hipError_t f = workspace_release(&ws, s);
     *done = true;
+    if (fixed) return e;
+    const hipError_t f = workspace_release(&ws, s);
     return e != hipSuccess ? e : f;
 }
 
@@ -406,33 +423,55 @@ static bool capturing(hipStream_t s) {
     return st != hipStreamCaptureStatusNone;
 }
 
-hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested) {
-    const bool in_graph = capturing(s);
-    if (requested == 0) {
+size_t k4_split_scratch_bytes(const GemmArgs& g, int requested) {
+    const SplitPlan p = k4_plan(g, requested);
+    return p.splits > 1 ? size_t(p.ws_floats) * sizeof(float) : 0;
+}
+
+hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested, bool thin_ok,
+                          const FixedScratch* fixed) {
+    // A fixed scratch needs no allocation and no ordering across streams,
+    // so captured calls may use it too.
+    const bool in_graph = !fixed && capturing(s);
+    if (requested == 0 && thin_ok) {
         ThinPlan t = thin_plan(g);
         if (t.kind != ThinPlan::NONE) {
             Workspace ws;
-            if (t.splits > 1 && (in_graph || workspace_acquire(size_t(t.ws_floats) * sizeof(float), s,
-                                                               &ws) != hipSuccess)) {
-                // Captured, or no workspace: one chunk gives the same product.
-                if (!in_graph) (void)hipGetLastError();
-                t.splits = 1;
-                t.kchunk = g.K;
+            float* buf = nullptr;
+            bool pooled = false;
+            if (t.splits > 1) {
+                const size_t bytes = size_t(t.ws_floats) * sizeof(float);
+                if (fixed) {
+                    if (bytes <= fixed->bytes) buf = fixed->ptr;
+                } else if (!in_graph) {
+                    if (workspace_acquire(bytes, s, &ws) == hipSuccess) {
+                        buf = static_cast<float*>(ws.ptr);
+                        pooled = true;
+                    } else {
+                        (void)hipGetLastError();
+                    }
+                }
+                // Captured, or no scratch: one chunk gives the same product.
+                if (!buf) {
+                    t.splits = 1;
+                    t.kchunk = g.K;
+                }
             }
-            const hipError_t e = launch_thin(g, t, static_cast<float*>(ws.ptr), s);
-            if (t.splits <= 1) return e;
+            const hipError_t e = launch_thin(g, t, buf, s);
+            if (!pooled) return e;
             const hipError_t f = workspace_release(&ws, s);
             return e != hipSuccess ? e : f;
         }
     }
     if (requested == 0 && !in_graph) {
         bool done;
-        const hipError_t e = launch_packed(g, s, &done);
+        const hipError_t e = launch_packed(g, s, &done, fixed);
         if (done || e != hipSuccess) return e;
     }
     SplitPlan p = k4_plan(g, requested);
-    if (in_graph) p.splits = 1;
+    if (in_graph || (fixed && size_t(p.ws_floats) * sizeof(float) > fixed->bytes)) p.splits = 1;
     if (p.splits <= 1) return launch_plan(g, p, nullptr, s);
+    if (fixed) return launch_plan(g, p, fixed->ptr, s);
     Workspace ws;
     if (workspace_acquire(size_t(p.ws_floats) * sizeof(float), s, &ws) != hipSuccess) {
         // No workspace: the unsplit kernel gives the same product.

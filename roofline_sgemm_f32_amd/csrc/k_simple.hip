@@ -1,20 +1,26 @@
-// The first rungs of the ladder: one output element per lane.
+// The first rungs of the ladder: one output element per lane.  Stages are
+// those of amittech.dev, "3.5 Project: tiled matrix multiplication".
 //
-//  k0  one lane per C element, consecutive lanes walk DOWN a column of C
-//      (amittech.dev, "3.5 Project: tiled matrix multiplication", stage 0):
-//      a wave's A reads and C writes are row-strided - the uncoalesced foil.
-//  k1  consecutive lanes walk ALONG a row of C (same page, stage 1): B reads
-//      and C writes are contiguous per wave and the A element is uniform
-//      across the wave.  On a 64-lane wavefront the workgroup is 64 x 4, so
-//      one wave covers 64 consecutive columns of one row (a 16 x 16 block
-//      would split a wave over four rows and four 64-byte segments).
-//  k2  the same page, stage 2: the workgroup stages a TILE x TILE block of A
-//      and of B in LDS per K step (zero-filled past the matrix edge), with a
-//      barrier after the loads and another before the next overwrite.
+//  k0  stage 0 ("the naive baseline"), re-derived for 64-lane waves: the 64
+//      lanes of a wave take 64 consecutive ROWS of one column of C (the
+//      workgroup's four waves four neighbouring columns).  Each k step of a
+//      wave then reads A from 64 different rows and each store writes 64
+//      different rows: 64 separate cache lines where one would do.  This is
+//      the uncoalesced foil.
+//  k1  stage 1 ("global memory coalescing"): the same four waves turned the
+//      other way, a wave's lanes along 64 consecutive COLUMNS of one row.  B
+//      reads and C writes are 256 contiguous bytes per wave and the A
+//      element is uniform across the wave (a 16 x 16 block, as on a 32-lane
+//      machine, would split a 64-lane wave over four rows).
+//  k2  stage 2 ("shared memory tiling"): per K step the workgroup stages a
+//      TILE x TILE piece of A and of B in LDS, one element per lane each,
+//      zero past the matrix edge, and every lane then runs TILE
+//      multiply-adds out of LDS; one barrier after staging, one before the
+//      next step overwrites the pieces.
 //
 //      LDS banking on gfx950: 64 banks of 4 bytes, and a wave's 64 lanes are
 //      served together.  A wave of the 32 x 32 workgroup covers two tile rows
-//      (lanes 0-31 row ty, lanes 32-63 row ty+1); with a row stride of 32
+//      (lanes 0-31 one row, lanes 32-63 the next); with a row stride of 32
 //      floats the two halves fall in banks b..b+31 and b+32..b+63, so the
 //      unpadded tile is already conflict-free, and its 128-byte aligned rows
 //      let the inner loop read A four floats at a time.  A wave of the
@@ -30,16 +36,18 @@ namespace sgemm {
 __global__ void __launch_bounds__(256)
 k0_naive(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
          const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-         int64_t tiles_m, int64_t tiles) {
-    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int64_t row = (t % tiles_m) * 16 + tx;  // x -> row
-        const int64_t col = (t / tiles_m) * 16 + ty;  // y -> column
-        if (row < M && col < N) {
-            float sum = 0.0f;
-            for (int64_t k = 0; k < K; k++) sum += A[row * lda + k] * B[k * ldb + col];
-            C[row * ldc + col] = sum;
-        }
+         int64_t blocks_m, int64_t blocks) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    // Workgroup block: 64 rows x 4 columns of C, walked over the grid.
+    for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+        const int64_t i = (blk % blocks_m) * 64 + lane;  // one row per lane
+        const int64_t j = (blk / blocks_m) * 4 + wave;   // one column per wave
+        if (i >= M || j >= N) continue;
+        const float* arow = A + i * lda;
+        const float* bcol = B + j;
+        float acc = 0.0f;
+        for (int64_t k = 0; k < K; k++) acc += arow[k] * bcol[k * ldb];
+        C[i * ldc + j] = acc;
     }
 }
 
@@ -64,28 +72,33 @@ k1_coalesced(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
     }
 }
 
-template <int TILE, int PAD>
-__global__ void __launch_bounds__(TILE * TILE)
+template <int T, int PAD>
+__global__ void __launch_bounds__(T * T)
 k2_lds(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
        const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-       int64_t tiles_n, int64_t tiles) {
-    __shared__ float As[TILE][TILE + PAD];
-    __shared__ float Bs[TILE][TILE + PAD];
-    const int tx = threadIdx.x % TILE, ty = threadIdx.x / TILE;
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int64_t row = (t / tiles_n) * TILE + ty;
-        const int64_t col = (t % tiles_n) * TILE + tx;
-        float sum = 0.0f;
-        for (int64_t k0 = 0; k0 < K; k0 += TILE) {
-            const int64_t ak = k0 + tx, bk = k0 + ty;
-            As[ty][tx] = (row < M && ak < K) ? A[row * lda + ak] : 0.0f;
-            Bs[ty][tx] = (bk < K && col < N) ? B[bk * ldb + col] : 0.0f;
-            __syncthreads();  // the tile is complete before anyone reads it
+       int64_t blocks_n, int64_t blocks) {
+    constexpr int LD = T + PAD;  // LDS row stride in floats
+    __shared__ __attribute__((aligned(16))) float sa[T * LD];
+    __shared__ __attribute__((aligned(16))) float sb[T * LD];
+    // The lane's output inside the T x T block; c is also the k offset it
+    // stages from A, r the one it stages from B.
+    const int r = threadIdx.x / T, c = threadIdx.x % T;
+    for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
+        const int64_t i = (blk / blocks_n) * T + r;
+        const int64_t j = (blk % blocks_n) * T + c;
+        const bool row_in = i < M, col_in = j < N;
+        const float* arow = A + (row_in ? i : 0) * lda;
+        float acc = 0.0f;
+        for (int64_t kt = 0; kt < K; kt += T) {
+            sa[r * LD + c] = row_in && kt + c < K ? arow[kt + c] : 0.0f;
+            sb[r * LD + c] = kt + r < K && col_in ? B[(kt + r) * ldb + j] : 0.0f;
+            __syncthreads();
+            const float* ar = sa + r * LD;
 #pragma unroll
-            for (int k = 0; k < TILE; k++) sum += As[ty][k] * Bs[k][tx];
-            __syncthreads();  // everyone is done before the next overwrite
+            for (int q = 0; q < T; q++) acc += ar[q] * sb[q * LD + c];
+            __syncthreads();
         }
-        if (row < M && col < N) C[row * ldc + col] = sum;
+        if (row_in && col_in) C[i * ldc + j] = acc;
     }
 }
 
@@ -139,7 +152,7 @@ hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta,
 }
 
 hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s) {
-    const int64_t tm = ceil_div(g.M, 16), tiles = tm * ceil_div(g.N, 16);
+    const int64_t tm = ceil_div(g.M, 64), tiles = tm * ceil_div(g.N, 4);
     hipLaunchKernelGGL(k0_naive, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K, g.A,
                        g.lda, g.B, g.ldb, g.C, g.ldc, tm, tiles);
     return hipGetLastError();

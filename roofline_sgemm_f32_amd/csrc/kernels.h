@@ -42,9 +42,25 @@ hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k1_coalesced(const GemmArgs& g, hipStream_t s);
 hipError_t launch_k2_lds(const GemmArgs& g, int tile, int pad, hipStream_t s);
 hipError_t launch_k3_regtile(const GemmArgs& g, hipStream_t s);
+// Scratch memory fixed by the caller (the static scratch of the entry point
+// that allocates nothing): when given, the launches use it in place of the
+// library's workspace, and a plan whose scratch does not fit in `bytes`
+// runs without it (unpacked, or unsplit).
+struct FixedScratch {
+    float* ptr = nullptr;
+    size_t bytes = 0;
+};
 // Tile size and K split chosen by shape; requested_splits > 0 asks for that
-// many K chunks (at most; 1 = never split).
-hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested_splits = 0);
+// many K chunks (at most; 1 = never split).  thin_ok: a shape-chosen call
+// (requested_splits == 0) may run the thin-product kernels on the vector
+// units (thin.hip); otherwise every product runs on the matrix cores.
+hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested_splits = 0,
+                          bool thin_ok = true, const FixedScratch* fixed = nullptr);
+// Bytes of scratch an eager call with this split request would use for its
+// partial products (requested_splits >= 2; 0 when the plan does not split).
+size_t k4_split_scratch_bytes(const GemmArgs& g, int requested_splits);
+// Devices the per-device tables (workspace, static scratch) can serve.
+constexpr int kMaxDevices = 64;
 // Plan of the matrix-core kernel for a shape: tile configuration (cfg, an
 // internal id) and K split, `splits` chunks of kchunk (the last one shorter)
 // whose partial products take ws_floats floats of workspace.

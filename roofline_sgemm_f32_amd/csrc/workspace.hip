@@ -20,7 +20,6 @@
 namespace sgemm {
 
 namespace {
-constexpr int kMaxDevices = 64;
 constexpr size_t kCacheMax = size_t(256) << 20;
 
 struct DeviceWorkspace {

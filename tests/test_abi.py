@@ -368,3 +368,34 @@ def test_plan_config_thin(lib):
     assert cfg((1 << 27) + 4, 1, 4)["engine"] == "mfma"
     # A split request bypasses the thin path.
     assert rs.split_plan(8, 16384, 16384, A_ptr=ALIGNED, B_ptr=ALIGNED, splits=1) == (1, 16384)
+
+
+def _no_gpu_visible():
+    """True when no GPU can run anything here: no KFD device node, and the
+    HIP runtime counts no device.  Only then may a valid call with fake
+    pointers reach the launch (which must then fail cleanly)."""
+    if os.path.exists("/dev/kfd"):
+        return False
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return True
+    n = ctypes.c_int(0)
+    rc = hip.hipGetDeviceCount(ctypes.byref(n))
+    return rc != 0 or n.value == 0
+
+
+def test_launch_failure_without_device(lib):
+    """A valid call whose launch fails (here: no GPU in the machine) returns
+    SGEMM_ERR_LAUNCH and records the HIP error; the process is not aborted."""
+    if not _no_gpu_visible():
+        pytest.skip("a GPU is visible: fake device pointers must not be launched on")
+    assert lib.sgemm_f32(64, 64, 64, PA, 64, PB, 64, PC, 64, None) == LAUNCH
+    err = lib.sgemm_last_hip_error()
+    assert err != 0
+    # The shape-chosen split path (it would use the workspace) fails the same way.
+    assert lib.sgemm_f32_ex_split(0, 0, 64, 64, 8192, 1.0, PA, 8192, PB, 64, 0.0, PC, 64, 0, None) == LAUNCH
+    for v in rs.VARIANTS.values():
+        assert call(v, 40, 40, 40) == LAUNCH
+    assert lib.sgemm_copy_f32(PB, PA, 1000, None) == LAUNCH
+    assert lib.sgemm_last_hip_error() == err

@@ -49,3 +49,17 @@ def test_row_gate_rejects_nan_and_accepts_exact_integers():
 def test_row_gate_single_row():
     A, B = _operands(1, 5, 3, 14)
     assert bench.row_gate(A, B)(A @ B)[0]
+
+
+def test_oracle_gate_checks_every_element():
+    """bench.oracle_gate (the CPU leg's full-product gate): a float32 product
+    passes, one wrong element anywhere fails."""
+    from roofline_sgemm_f32_amd.inputs import Workload
+    A, B = _operands(23, 31, 200, 15)
+    w = Workload("t", 23, 31, 200, 200, 31, 31, "uniform", 15)
+    C = (A @ B).numpy()
+    rep = bench.oracle_gate(w, A, B, C)
+    assert rep["ok"] and rep["elements_checked"] == 23 * 31
+    C[11, 17] += 0.05
+    rep = bench.oracle_gate(w, A, B, C)
+    assert not rep["ok"] and rep["n_violations"] == 1
