@@ -30,8 +30,9 @@
  *
  *   The caller-owns-everything reading of the course's scaffolding (the
  *   harness allocates every buffer) holds for sgemm_f32_variant with the
- *   ladder variants 1-3, 5-8 and 9-11 and for the copy and compute probes:
- *   they allocate no device memory and never synchronise.  The shape-chosen paths depart from it in one place, a
+ *   ladder variants 1-3, 5-8 and 9-11, for the copy and compute probes, and
+ *   for sgemm_f32_ex_split_noalloc: they allocate no device memory and never
+ *   synchronise.  The shape-chosen paths depart from it in one place, a
  *   library workspace:
  *     - sgemm_f32 and SGEMM_AUTO, SGEMM_K4_MFMA, sgemm_f32_ex,
  *       sgemm_f32_colmajor and sgemm_f32_ex_split use scratch device memory
@@ -121,7 +122,9 @@ typedef enum sgemm_status {
     SGEMM_ERR_ALIAS = 5,       /* C's byte range overlaps A's or B's */
     SGEMM_ERR_LAUNCH = 6,      /* the HIP launch failed (see sgemm_last_hip_error) */
     SGEMM_ERR_UNSUPPORTED = 7, /* the explicit variant cannot index this shape (AUTO always can) */
-    SGEMM_ERR_ARG = 8          /* another invalid argument (copy probe: n < 0, bad block or grid) */
+    SGEMM_ERR_ARG = 8,         /* another invalid argument (copy probe: n < 0, bad block or grid) */
+    SGEMM_ERR_SCRATCH = 9      /* sgemm_f32_ex_split_noalloc: the requested K split's partial
+                                  products need more than SGEMM_STATIC_SCRATCH_BYTES */
 } sgemm_status_t;
 
 /* C = A * B with the variant chosen per shape.  Same as
@@ -182,6 +185,29 @@ int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float 
 int sgemm_f32_ex_split(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
                        const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
                        float *C, int64_t ldc, int splits, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation and arguments as sgemm_f32_ex_split, with the library's static
+ * device scratch in place of its workspace.  It calls no allocator and
+ * never synchronises, captured or not.
+ *   The scratch is a static device array of SGEMM_STATIC_SCRATCH_BYTES that
+ *   every device the library runs on holds until the process ends.
+ *   splits == 0 or 1: the shape's plan, except that packing, a K split or a
+ *   thin product's split runs only when its scratch fits (otherwise the same
+ *   product runs unpacked or unsplit, on the matrix cores or the thin
+ *   kernels as chosen);
+ *   2 <= splits <= SGEMM_MAX_SPLITS: partial products that would exceed the
+ *   scratch give SGEMM_ERR_SCRATCH before any HIP call.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents (nothing in it needs to start at zero); calls that overlap
+ * in time on one device (from different streams or threads) race on it, so
+ * a caller issues them on one stream or orders them itself. */
+#define SGEMM_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+int sgemm_f32_ex_split_noalloc(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float *A, int64_t lda, const float *B,
+                               int64_t ldb, float beta, float *C, int64_t ldc, int splits,
+                               void *stream);
 
 /* The K split sgemm_f32_ex_split(transa, transb, M, N, K, ..., splits, ...)
  * would run with these operands (host-only decision, no HIP call; the

@@ -33,16 +33,17 @@ VARIANTS = {
 STATUS = {
     0: "SGEMM_OK", 1: "SGEMM_ERR_DIM", 2: "SGEMM_ERR_LD", 3: "SGEMM_ERR_NULLPTR",
     4: "SGEMM_ERR_VARIANT", 5: "SGEMM_ERR_ALIAS", 6: "SGEMM_ERR_LAUNCH",
-    7: "SGEMM_ERR_UNSUPPORTED", 8: "SGEMM_ERR_ARG",
+    7: "SGEMM_ERR_UNSUPPORTED", 8: "SGEMM_ERR_ARG", 9: "SGEMM_ERR_SCRATCH",
 }
 
 EXPORTS = ["sgemm_f32", "sgemm_f32_variant", "sgemm_copy_f32", "sgemm_copy_f32_launch",
            "sgemm_status_string", "sgemm_variant_name", "sgemm_auto_variant",
            "sgemm_last_hip_error", "sgemm_abi_version", "sgemm_probe_valu_f32",
            "sgemm_probe_mfma_f32", "sgemm_f32_ex", "sgemm_f32_colmajor", "sgemm_f32_ex_split",
-           "sgemm_split_plan", "sgemm_plan_config"]
+           "sgemm_split_plan", "sgemm_plan_config", "sgemm_f32_ex_split_noalloc"]
 
 MAX_SPLITS = 64
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024  # SGEMM_STATIC_SCRATCH_BYTES
 
 OP_N, OP_T = 0, 1
 
@@ -81,6 +82,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_f32_colmajor.restype = cint
     lib.sgemm_f32_ex_split.argtypes = [*ex[:-1], cint, vp]
     lib.sgemm_f32_ex_split.restype = cint
+    lib.sgemm_f32_ex_split_noalloc.argtypes = [*ex[:-1], cint, vp]
+    lib.sgemm_f32_ex_split_noalloc.restype = cint
     lib.sgemm_split_plan.argtypes = [cint, cint, i64, i64, i64, vp, i64, vp, i64, cint,
                                      ctypes.POINTER(i64)]
     lib.sgemm_split_plan.restype = cint
@@ -176,13 +179,16 @@ def sgemm(A, B, out=None, variant="auto"):
     return out
 
 
-def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0, splits=None):
+def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0, splits=None,
+             noalloc=False):
     """C = alpha op(A) op(B) + beta C (row-major float32 GPU tensors).  A is
     M x K, or K x M with transa (op(A) = A^T); B is K x N, or N x K with
     transb.  ``out`` holds C (read only when beta != 0); it is allocated when
     omitted (then beta must be 0).  ``splits`` (sgemm_f32_ex_split): None or
     0 chooses the K split by shape, 1 never splits, 2..64 asks for at most
-    that many K chunks."""
+    that many K chunks.  ``noalloc`` calls sgemm_f32_ex_split_noalloc, whose
+    scratch is the library's static device array (the library then
+    allocates nothing)."""
     import torch
     if A.device.type != "cuda" or B.device.type != "cuda":
         raise ValueError("operands must be GPU tensors")
@@ -198,7 +204,10 @@ def sgemm_ex(A, B, out=None, transa=False, transb=False, alpha=1.0, beta=0.0, sp
         raise ValueError("out has the wrong shape")
     args = (int(transa), int(transb), M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(),
             _ld(B, "B"), beta, out.data_ptr(), _ld(out, "out"))
-    if splits is None:
+    if noalloc:
+        name = "sgemm_f32_ex_split_noalloc"
+        st = load().sgemm_f32_ex_split_noalloc(*args, int(splits or 0), _stream_handle(A.device))
+    elif splits is None:
         name = "sgemm_f32_ex"
         st = load().sgemm_f32_ex(*args, _stream_handle(A.device))
     else:

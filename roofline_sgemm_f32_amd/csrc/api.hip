@@ -154,6 +154,34 @@ int sgemm_f32_ex_split(int transa, int transb, int64_t M, int64_t N, int64_t K, 
     return launch_status(sgemm::launch_k1_general(g, s));
 }
 
+int sgemm_f32_ex_split_noalloc(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float* A, int64_t lda, const float* B,
+                               int64_t ldb, float beta, float* C, int64_t ldc, int splits,
+                               void* stream) {
+    static_assert(sgemm::kStaticScratchBytes == size_t(SGEMM_STATIC_SCRATCH_BYTES),
+                  "header and library agree on the static scratch size");
+    if (splits < 0 || splits > SGEMM_MAX_SPLITS) return SGEMM_ERR_ARG;
+    const int v = validate_ex(transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (v != SGEMM_OK) return v;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f) return launch_status(sgemm::launch_scale(C, M, N, ldc, beta, s));
+    GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
+    g.trans_a = transa == SGEMM_OP_T;
+    g.trans_b = transb == SGEMM_OP_T;
+    g.alpha = alpha;
+    g.beta = beta;
+    if (!sgemm::k4_supports(g)) return launch_status(sgemm::launch_k1_general(g, s));
+    // An explicit split whose partial products exceed the scratch is refused
+    // before any HIP call.
+    if (splits >= 2 && sgemm::k4_split_scratch_bytes(g, splits) > sgemm::kStaticScratchBytes)
+        return SGEMM_ERR_SCRATCH;
+    sgemm::FixedScratch fs;
+    const hipError_t e = sgemm::static_scratch(s, &fs);
+    if (e != hipSuccess) return launch_status(e);
+    return launch_status(sgemm::launch_k4_mfma(g, s, splits, true, &fs));
+}
+
 int sgemm_f32_ex(int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
                  const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                  int64_t ldc, void* stream) {
@@ -262,6 +290,7 @@ const char* sgemm_status_string(int status) {
         case SGEMM_ERR_LAUNCH: return "kernel launch failed";
         case SGEMM_ERR_UNSUPPORTED: return "variant cannot address this shape";
         case SGEMM_ERR_ARG: return "invalid argument";
+        case SGEMM_ERR_SCRATCH: return "the requested split needs more than the static scratch holds";
         default: return "unknown status";
     }
 }

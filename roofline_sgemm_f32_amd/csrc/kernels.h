@@ -61,6 +61,11 @@ hipError_t launch_k4_mfma(const GemmArgs& g, hipStream_t s, int requested_splits
 size_t k4_split_scratch_bytes(const GemmArgs& g, int requested_splits);
 // Devices the per-device tables (workspace, static scratch) can serve.
 constexpr int kMaxDevices = 64;
+// Size of the library's static device scratch (static_scratch.hip).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+// The static scratch of the device that runs `s`: its device address (found
+// once per device) and size.
+hipError_t static_scratch(hipStream_t s, FixedScratch* out);
 // Plan of the matrix-core kernel for a shape: tile configuration (cfg, an
 // internal id) and K split, `splits` chunks of kchunk (the last one shorter)
 // whose partial products take ws_floats floats of workspace.

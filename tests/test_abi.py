@@ -11,7 +11,7 @@ import roofline_sgemm_f32_amd as rs
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgemm.h")
 
-OK, DIM, LD, NULLPTR, VARIANT, ALIAS, LAUNCH, UNSUPPORTED, ARG = range(9)
+OK, DIM, LD, NULLPTR, VARIANT, ALIAS, LAUNCH, UNSUPPORTED, ARG, SCRATCH = range(10)
 
 # Distinct, non-overlapping fake device addresses: validation never
 # dereferences them and returns before any HIP call.
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_and_variant_names(lib):
     assert rs.status_string(OK) == "ok"
-    for s in range(1, 9):
+    for s in range(1, 10):
         assert rs.status_string(s) not in ("ok", "unknown status")
     assert rs.status_string(1234) == "unknown status"
     for name, vid in rs.VARIANTS.items():
@@ -395,7 +395,27 @@ def test_launch_failure_without_device(lib):
     assert err != 0
     # The shape-chosen split path (it would use the workspace) fails the same way.
     assert lib.sgemm_f32_ex_split(0, 0, 64, 64, 8192, 1.0, PA, 8192, PB, 64, 0.0, PC, 64, 0, None) == LAUNCH
+    assert lib.sgemm_f32_ex_split_noalloc(0, 0, 64, 64, 8192, 1.0, PA, 8192, PB, 64, 0.0, PC, 64, 0,
+                                          None) == LAUNCH
     for v in rs.VARIANTS.values():
         assert call(v, 40, 40, 40) == LAUNCH
     assert lib.sgemm_copy_f32(PB, PA, 1000, None) == LAUNCH
     assert lib.sgemm_last_hip_error() == err
+
+
+def test_noalloc_validation(lib):
+    f = lib.sgemm_f32_ex_split_noalloc
+    args = (0, 0, 64, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64)
+    assert f(*args, -1, None) == ARG
+    assert f(*args, rs.MAX_SPLITS + 1, None) == ARG
+    assert f(2, 0, 64, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, None) == ARG
+    assert f(0, 0, -1, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, None) == DIM
+    assert f(0, 0, 64, 64, 64, 1.0, PA, 32, PB, 64, 0.0, PC, 64, 0, None) == LD
+    assert f(0, 0, 64, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PA + 4, 64, 0, None) == ALIAS
+    assert f(0, 0, 0, 64, 64, 1.0, None, 64, None, 64, 0.0, None, 64, 0, None) == OK
+    # Two chunks of 4096 x 4096 partial products: 128 MiB, over the 64 MiB
+    # static scratch; refused on the host, before any HIP call.
+    assert rs.STATIC_SCRATCH_BYTES == 64 << 20
+    big = (0, 0, 4096, 4096, 8192, 1.0, PA, 8192, PB, 4096, 0.0, PC, 4096)
+    assert f(*big, 2, None) == SCRATCH
+    assert rs.status_string(SCRATCH) != "unknown status"
