@@ -15,13 +15,13 @@ Legs, in the order they run:
   * hbm_copy: the copy probe (256 Mi floats, 2 GiB moved) against 8 TB/s,
     and compute_probe: register-only FMA chains and back-to-back FP32 matrix
     instructions, the two roofs the kernels are measured against.
+  * configs: each of the five workloads through AUTO (time per call,
+    GFLOP/s, fraction of the FP32 peak).
   * GPU product (the headline): value = 2 M N K / mean step time.
   * roofline: the matrix-core kernel's achieved TFLOP/s against 157.3, from
     the events around the timed launches on the launch stream; ``traffic``
     is read from a committed counter summary when it was taken on the
     current kernel source.
-  * configs: each of the five workloads through AUTO (time per call,
-    GFLOP/s, fraction of the FP32 peak).
   * small_shapes: the small-shape path, split as chosen and unsplit.
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the headline product; the oracle's full results then gate every element
@@ -235,8 +235,8 @@ def oracle_gate(w, A_h, B_h, C_host):
 def configs_leg(budget_s: float):
     """The five workloads through AUTO: back-to-back calls for about
     ``budget_s`` (at least 20, after as many warm-ups), mean per call.
-    Returns the records and, per workload, the host operands and the host
-    copy of the timed launches' result for the CPU leg's gate."""
+    Returns the records and, per workload, the host operands and the
+    (device) result of the timed launches, for the CPU leg's gate."""
     import torch
     import roofline_sgemm_f32_amd as rs
     from roofline_sgemm_f32_amd import metrics as m
@@ -261,11 +261,10 @@ def configs_leg(budget_s: float):
                "ms": round(ms, 5), "gflops": round(g, 1),
                "pct_peak": round(m.pct_of_peak(g, m.MI355X_FP32_PEAK_GFLOPS), 2), "steps": steps}
         rows.append(rec)
-        keep[name] = (w, A_h, B_h, C.cpu().numpy())
+        keep[name] = (w, A_h, B_h, C)
         log(f"  config {name:22s} {ms:9.4f} ms {g:10.1f} GFLOP/s {rec['pct_peak']:6.2f}% "
             f"tile {plan['tile']} x{plan['k_groups']} packed={plan['packed']} chunks={plan['splits']}")
-        del A, B, C
-        torch.cuda.empty_cache()
+        del A, B
     return rows, keep
 
 
@@ -302,9 +301,9 @@ def compute_probe(valu_iters=4096, mfma_iters=4096, steps=30, warmup=10):
     import roofline_sgemm_f32_amd as rs
     from roofline_sgemm_f32_amd.inputs import probe_operands
     blocks, block = 256 * 8, 256  # 32 waves per CU
-    out_v = torch.empty((blocks * block, 16), device="cuda")
+    out_v = torch.empty((blocks * block, rs.VALU_CHAINS), device="cuda")
     tv = launch_times(lambda: rs.probe_valu(blocks, block, valu_iters, 0.999, 0.001, out_v), steps, warmup)
-    fv = blocks * block * valu_iters * 16 * 2
+    fv = blocks * block * valu_iters * rs.VALU_CHAINS * 2
     a, b = probe_operands(7)
     a, b = a.cuda(), b.cuda()
     # 8 waves per CU (2 per SIMD): with 4 per SIMD the back-to-back MFMA
@@ -571,20 +570,8 @@ def main():
                                                        args.small_only.split(","))}), flush=True)
         return
 
-    # The roofs first: the copy probe and the compute probes calibrate the
-    # denominators the kernels are measured against.  (They also leave the
-    # GPU clock up: on a cold GPU the first ~0.1 s of launches run up to
-    # 25 % slower while the clock rises.)
-    copy = copy_probe(args.copy_steps) if args.copy_steps > 0 else None
-    if copy:
-        log(f"[bench] copy probe {copy['gbs']} GB/s ({100 * copy['frac']:.1f}% of 8 TB/s)")
-    probe = compute_probe() if args.compute_probe else None
-    if probe:
-        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s "
-            f"(best {probe['valu_fma_tflops_best']}), FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s "
-            f"(best {probe['mfma_f32_tflops_best']})")
-    torch.cuda.empty_cache()
-
+    # The headline's operands are drawn and placed first, so that no host
+    # work separates the probe legs from its launches.
     w = WORKLOADS[args.workload]
     A_h, B_h, A, B, C = device_operands(w)
     variant = args.variant
@@ -593,6 +580,22 @@ def main():
         resolved = rs.variant_name(rs.load().sgemm_auto_variant(
             w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, C.data_ptr(), w.ldc))
     fn = run_gemm_factory(variant, A, B, C)
+
+    # The roofs first: the copy probe and the compute probes calibrate the
+    # denominators the kernels are measured against.  Then the configs
+    # section (the five workloads through AUTO), and the headline directly
+    # after it.  The order matters for a headline of few warm-ups: square4096
+    # launches settle at 0.961 ms, but start at 1.12-1.19 ms after 1 s of GPU
+    # idleness (the clock ramps up over ~25 ms of load) and at 1.07 ms right
+    # after the matrix-core probe (it runs the chip harder than the product
+    # does, and the clock recovers over ~25 launches), while right after
+    # other products of this kind the first launch already takes 0.966 ms
+    # (MI355X, fresh processes).  The first launch of a kernel in a process
+    # also carries its code object's loading (about 3 ms), which the
+    # configs section pays instead of the headline's warm-ups.
+    copy = copy_probe(args.copy_steps) if args.copy_steps > 0 else None
+    probe = compute_probe() if args.compute_probe else None
+    configs, keep = (configs_leg(args.configs_seconds) if args.configs_seconds > 0 else (None, {}))
     log(f"[bench] {w.name} {w.M}x{w.N}x{w.K} variant={variant} ({resolved}) "
         f"warmup={args.warmup} steps={args.steps}")
     # The timed region is the K back-to-back launches between two events on
@@ -605,6 +608,12 @@ def main():
     peak_tf = m.MI355X_FP32_PEAK_GFLOPS / 1e3
     log(f"[bench] {ms_step:.4f} ms/step, {value:.1f} GFLOP/s, "
         f"{m.pct_of_peak(value, m.MI355X_FP32_PEAK_GFLOPS):.2f}% of FP32 peak")
+    if copy:
+        log(f"[bench] copy probe {copy['gbs']} GB/s ({100 * copy['frac']:.1f}% of 8 TB/s)")
+    if probe:
+        log(f"[bench] compute probe: FP32 FMA chains {probe['valu_fma_tflops']} TFLOP/s "
+            f"(best {probe['valu_fma_tflops_best']}), FP32 MFMA {probe['mfma_f32_tflops']} TFLOP/s "
+            f"(best {probe['mfma_f32_tflops_best']})")
     # The timed launches' result, checked by the CPU leg.
     C_host = C.cpu().numpy()
     del A, B, C
@@ -620,7 +629,6 @@ def main():
                     out.write(json.dumps({"copy_sweep": r}) + "\n")
     if args.ladder:
         ladder(args, out)
-    configs, keep = (configs_leg(args.configs_seconds) if args.configs_seconds > 0 else (None, {}))
     small = small_shapes(args.small_reps) if args.small_reps > 0 else None
 
     # The CPU leg runs last: the GPU clock falls during its seconds of GPU
@@ -633,7 +641,7 @@ def main():
         log(f"[bench] oracle {cpu['value']} GFLOP/s; gate {gate}")
         for rec in configs or []:
             cw, ca, cb, cc = keep[rec["workload"]]
-            rec["gate"] = oracle_gate(cw, ca, cb, cc)
+            rec["gate"] = oracle_gate(cw, ca, cb, cc.cpu().numpy())
             if not rec["gate"]["ok"]:
                 rec["gflops"] = rec["pct_peak"] = None
             log(f"  gate {rec['workload']:22s} {rec['gate']}")
@@ -664,6 +672,7 @@ def main():
                      "flops_per_launch": flops, "ms_per_launch": round(ms_launch, 5)},
         "cpu_baseline": cpu,
         "gate": gate,
+        "headline_preceded_by": ["hbm_copy", "compute_probe"] + (["configs"] if configs else []),
         "hbm_copy": copy,
         "compute_probe": probe,
         "configs": configs,

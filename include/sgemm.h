@@ -273,11 +273,11 @@ int sgemm_copy_f32_launch(float *dst, const float *src, int64_t n,
  * sustained arithmetic rate).
  *
  * sgemm_probe_valu_f32: blocks x block lanes (block a multiple of 64 in
- * 64..1024, blocks in 1..2^20); lane t runs 16 independent chains, chain j
- * starting at (j + 1) / 16 and updated iters times as acc = fmaf(acc, x, y),
- * and writes the 16 final values to out[16 t .. 16 t + 15].  out is a device
- * buffer of blocks * block * 16 floats owned by the caller.  Work:
- * blocks * block * iters * 16 * 2 FLOP.
+ * 64..1024, blocks in 1..2^20); lane t runs 32 independent chains, chain j
+ * starting at (j + 1) / 16 and updated iters times as acc = fmaf(acc, x, y)
+ * with x and y held in vector registers, and writes the 32 final values to
+ * out[32 t .. 32 t + 31].  out is a device buffer of blocks * block * 32
+ * floats owned by the caller.  Work: blocks * block * iters * 32 * 2 FLOP.
  *
  * sgemm_probe_mfma_f32: blocks workgroups of 4 waves (1..2^20).  Every wave
  * accumulates iters products A * B (A 32 x 2 with A[i][k] = a_vals[i + 32 k],

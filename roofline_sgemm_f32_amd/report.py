@@ -59,6 +59,8 @@ def parse_counter_table(path: str) -> list[Point]:
     pts = []
     with open(path) as f:
         for ln in f:
+            if ln.startswith("# Wave-cycle breakdown"):
+                break  # the stall section that follows has columns of its own
             if ln.startswith("#") or ln.startswith("kernel") or not ln.strip():
                 continue
             cols = ln.split()

@@ -31,9 +31,9 @@ def test_valu_probe_matches_oracle(x, y, iters, blocks, block):
     print(f"[probe-valu] x={x} y={y} iters={iters} blocks={blocks} block={block}", flush=True)
     out = rs.probe_valu(blocks, block, iters, x, y)
     torch.cuda.synchronize()
-    want = oracle.fma_chain_f32(iters, x, y, 16)
+    want = oracle.fma_chain_f32(iters, x, y, rs.VALU_CHAINS)
     got = out.cpu().numpy()
-    assert got.shape == (blocks * block, 16)
+    assert got.shape == (blocks * block, rs.VALU_CHAINS)
     assert np.array_equal(got, np.tile(want, (blocks * block, 1)))
 
 
