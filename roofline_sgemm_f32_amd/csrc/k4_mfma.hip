@@ -108,8 +108,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     // or slab offsets do not fit (k4_supports) to the 64-bit kernel.
     constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH;
     constexpr int WG_WAVES = CF::NWAVES;  // waves of one K group
-    // Partial accumulators of groups 1.. WK-1, one float per lane and register.
-    constexpr int RED_BYTES = (WK - 1) * WG_WAVES * TM * TN * 16 * 64 * 4;
+    // The K groups' partial tiles, rows padded to BN + 8 floats (WK > 1).
+    constexpr int RLD = CF::BN + 8;
+    constexpr int RED_BYTES = WK > 1 ? WK * CF::BM * RLD * 4 : 0;
     constexpr int LDS_TOTAL = CF::LDS_BYTES * WK > RED_BYTES ? CF::LDS_BYTES * WK : RED_BYTES;
     static_assert(WK >= 1 && WK <= 8 && CF::THREADS * WK <= 1024, "K groups");
     static_assert(LDS_TOTAL <= 160 * 1024, "LDS per workgroup");
@@ -342,41 +343,61 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         }
         for (; s < iters; s++) slab_step(s, std::true_type{});
 
+        const bool read_c = beta != 0.0f;
         if constexpr (WK > 1) {
-            // Every stage is free after the loop's last barrier: groups
-            // 1 .. WK-1 leave their accumulators there, group 0 adds them in
-            // group order.
+            // Every stage is free after the loop's last barrier.  Each K group
+            // leaves its partial tile in LDS (a row of BN floats plus 8, so
+            // the two halves of a wave's accumulator writes, four rows apart,
+            // fall on disjoint banks); then every lane of the workgroup adds
+            // four neighbouring outputs over the groups, in group order, and
+            // stores them, 16 bytes at a time where C allows.  (Group 0 alone
+            // adding and storing the tile took about 1.6 us of the 23 us of
+            // square 1024.)
+            constexpr int PER_LANE = CF::BM * CF::BN / (CF::THREADS * WK);
+            static_assert(PER_LANE == 4, "four outputs per lane");
             float* red = reinterpret_cast<float*>(smem);
-            auto slot = [&](int g, int mb, int nb, int r) {
-                return ((((g - 1) * WG_WAVES + wave) * TM + mb) * TN * 16 + nb * 16 + r) * 64 + lane;
-            };
-            if (kg > 0) {
 #pragma unroll
-                for (int mb = 0; mb < TM; mb++)
+            for (int mb = 0; mb < TM; mb++)
 #pragma unroll
-                    for (int nb = 0; nb < TN; nb++)
+                for (int nb = 0; nb < TN; nb++)
 #pragma unroll
-                        for (int r = 0; r < 16; r++) red[slot(kg, mb, nb, r)] = acc[mb][nb][r];
-            }
+                    for (int r = 0; r < 16; r++) {
+                        const int row = wm * TM * 32 + mb * 32 + (r / 4) * 8 + ls * 4 + r % 4;
+                        const int col = wn * TN * 32 + nb * 32 + li;
+                        red[(kg * CF::BM + row) * RLD + col] = acc[mb][nb][r];
+                    }
             __syncthreads();
-            if (kg == 0) {
-                for (int g = 1; g < WK; g++)
+            const int row = tid * 4 / CF::BN, col = tid * 4 % CF::BN;
+            v4f sum = *(const v4f*)(red + row * RLD + col);
 #pragma unroll
-                    for (int mb = 0; mb < TM; mb++)
-#pragma unroll
-                        for (int nb = 0; nb < TN; nb++)
-#pragma unroll
-                            for (int r = 0; r < 16; r++) acc[mb][nb][r] += red[slot(g, mb, nb, r)];
-            }
+            for (int g = 1; g < WK; g++) sum += *(const v4f*)(red + (g * CF::BM + row) * RLD + col);
             __syncthreads();  // the next tile's loads reuse this memory
-            if (kg > 0) continue;
+            const int gr = row0 + row, gc = col0 + col;
+            float* cp = C + (int64_t)gr * ldc + gc;
+            const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
+            if (tile_inside && !read_c && vec_c) {
+                v4f v;
+#pragma unroll
+                for (int e = 0; e < 4; e++) v[e] = alpha * sum[e];
+                if constexpr (SPLITK) *(v4f*)cp = v;
+                else __builtin_nontemporal_store(v, (v4f*)cp);
+            } else if (gr < M) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if (gc + e < N) {
+                        float v = alpha * sum[e];
+                        if (read_c) v = fmaf(beta, cp[e], v);
+                        cp[e] = v;
+                    }
+                }
+            }
+            continue;
         }
 
         // Accumulator register r of lane L holds row 8*(r/4) + 4*(L/32) + r%4,
         // column L%32 of its 32 x 32 block.  C = alpha * acc (+ beta * C when
         // beta is nonzero; C is not read otherwise).
         const bool interior = tile_inside;
-        const bool read_c = beta != 0.0f;
 #pragma unroll
         for (int mb = 0; mb < TM; mb++)
 #pragma unroll
