@@ -354,7 +354,8 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             // adding and storing the tile took about 1.6 us of the 23 us of
             // square 1024.)
             constexpr int PER_LANE = CF::BM * CF::BN / (CF::THREADS * WK);
-            static_assert(PER_LANE == 4, "four outputs per lane");
+            static_assert(PER_LANE % 4 == 0 && PER_LANE * CF::THREADS * WK == CF::BM * CF::BN,
+                          "whole 16-byte chunks per lane");
             float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
             for (int mb = 0; mb < TM; mb++)
@@ -367,27 +368,35 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                         red[(kg * CF::BM + row) * RLD + col] = acc[mb][nb][r];
                     }
             __syncthreads();
-            const int row = tid * 4 / CF::BN, col = tid * 4 % CF::BN;
-            v4f sum = *(const v4f*)(red + row * RLD + col);
+            v4f sum[PER_LANE / 4];
 #pragma unroll
-            for (int g = 1; g < WK; g++) sum += *(const v4f*)(red + (g * CF::BM + row) * RLD + col);
+            for (int q = 0; q < PER_LANE / 4; q++) {
+                const int o = (tid + q * CF::THREADS * WK) * 4, row = o / CF::BN, col = o % CF::BN;
+                sum[q] = *(const v4f*)(red + row * RLD + col);
+#pragma unroll
+                for (int g = 1; g < WK; g++) sum[q] += *(const v4f*)(red + (g * CF::BM + row) * RLD + col);
+            }
             __syncthreads();  // the next tile's loads reuse this memory
-            const int gr = row0 + row, gc = col0 + col;
-            float* cp = C + (int64_t)gr * ldc + gc;
             const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
-            if (tile_inside && !read_c && vec_c) {
-                v4f v;
 #pragma unroll
-                for (int e = 0; e < 4; e++) v[e] = alpha * sum[e];
-                if constexpr (SPLITK) *(v4f*)cp = v;
-                else __builtin_nontemporal_store(v, (v4f*)cp);
-            } else if (gr < M) {
+            for (int q = 0; q < PER_LANE / 4; q++) {
+                const int o = (tid + q * CF::THREADS * WK) * 4;
+                const int gr = row0 + o / CF::BN, gc = col0 + o % CF::BN;
+                float* cp = C + (int64_t)gr * ldc + gc;
+                if (tile_inside && !read_c && vec_c) {
+                    v4f v;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    if (gc + e < N) {
-                        float v = alpha * sum[e];
-                        if (read_c) v = fmaf(beta, cp[e], v);
-                        cp[e] = v;
+                    for (int e = 0; e < 4; e++) v[e] = alpha * sum[q][e];
+                    if constexpr (SPLITK) *(v4f*)cp = v;
+                    else __builtin_nontemporal_store(v, (v4f*)cp);
+                } else if (gr < M) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        if (gc + e < N) {
+                            float v = alpha * sum[q][e];
+                            if (read_c) v = fmaf(beta, cp[e], v);
+                            cp[e] = v;
+                        }
                     }
                 }
             }
