@@ -34,6 +34,13 @@
 // MFMA operand k-slots: lane L of the 32x32x2 instruction supplies A[L%32][s]
 // and B[s][L%32], s = L/32.  Slot s at step t (t < BK/2) stands for slab
 // column k = s*BK/2 + t.
+//
+// Columns of a wave's accumulator blocks: block nb's column j (the lane's
+// L%32) is tile column wn*TN*32 + nb*32 + j, except with B stored K x N and
+// TN = 4 (B_INTERLEAVE), where it is wn*TN*32 + 4*j + nb: the four blocks
+// interleave, so a lane's four B values of one k are 16 contiguous bytes of
+// a KRows row (one ds_read_b128) and its four outputs of one row are 16
+// contiguous bytes of C.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -130,8 +137,14 @@ struct Cfg {
     static_assert(LA::INSTR % NWAVES == 0 && LB::INSTR % NWAVES == 0, "loads split evenly over waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 
+    static constexpr bool B_INTERLEAVE = !B_KMAJOR && TN == 4;
     // Slab column that k-slot s stands for at MFMA step t.
     __host__ __device__ static constexpr int kslot(int s, int t) { return s * KH + t; }
+    // Tile row and column of a wave's accumulator blocks (lane index j = L%32).
+    __host__ __device__ static constexpr int a_row(int wm, int mb, int j) { return wm * TM * 32 + mb * 32 + j; }
+    __host__ __device__ static constexpr int b_col(int wn, int nb, int j) {
+        return B_INTERLEAVE ? wn * TN * 32 + 4 * j + nb : wn * TN * 32 + nb * 32 + j;
+    }
     // Stage bytes of A(m, k) and B(k, n) for tile-local m, n, k.
     __host__ __device__ static constexpr int a_elem(int m, int k) {
         if constexpr (A_KMAJOR) return A_BASE + LA::elem(m, k);

@@ -253,7 +253,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             auto read_frags = [&](int h, float (&af)[TM][KP], float (&bf)[TN][KP]) {
 #pragma unroll
                 for (int mb = 0; mb < TM; mb++) {
-                    const int row = wm * TM * 32 + mb * 32 + li;
+                    const int row = CF::a_row(wm, mb, li);
                     if constexpr (CF::A_KMAJOR) {
 #pragma unroll
                         for (int q = 0; q < KP / 4; q++) {
@@ -267,20 +267,30 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                             af[mb][u] = *(const float*)(st + CF::a_elem(row, CF::kslot(ls, h * KP + u)));
                     }
                 }
+                if constexpr (CF::B_INTERLEAVE) {
+                    // The lane's four columns of one k: one 16-byte read.
 #pragma unroll
-                for (int nb = 0; nb < TN; nb++) {
-                    const int col = wn * TN * 32 + nb * 32 + li;
-                    if constexpr (CF::B_KMAJOR) {
+                    for (int u = 0; u < KP; u++) {
+                        const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), CF::b_col(wn, 0, li)));
 #pragma unroll
-                        for (int q = 0; q < KP / 4; q++) {
-                            const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, h * KP + 4 * q), col));
+                        for (int nb = 0; nb < TN; nb++) bf[nb][u] = v[nb];
+                    }
+                } else {
 #pragma unroll
-                            for (int e = 0; e < 4; e++) bf[nb][4 * q + e] = v[e];
+                    for (int nb = 0; nb < TN; nb++) {
+                        const int col = CF::b_col(wn, nb, li);
+                        if constexpr (CF::B_KMAJOR) {
+#pragma unroll
+                            for (int q = 0; q < KP / 4; q++) {
+                                const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, h * KP + 4 * q), col));
+#pragma unroll
+                                for (int e = 0; e < 4; e++) bf[nb][4 * q + e] = v[e];
+                            }
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < KP; u++)
+                                bf[nb][u] = *(const float*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), col));
                         }
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < KP; u++)
-                            bf[nb][u] = *(const float*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), col));
                     }
                 }
             };
@@ -363,8 +373,8 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                 for (int nb = 0; nb < TN; nb++)
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
-                        const int row = wm * TM * 32 + mb * 32 + (r / 4) * 8 + ls * 4 + r % 4;
-                        const int col = wn * TN * 32 + nb * 32 + li;
+                        const int row = CF::a_row(wm, mb, 0) + (r / 4) * 8 + ls * 4 + r % 4;
+                        const int col = CF::b_col(wn, nb, li);
                         red[(kg * CF::BM + row) * RLD + col] = acc[mb][nb][r];
                     }
             __syncthreads();
@@ -407,12 +417,44 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         // column L%32 of its 32 x 32 block.  C = alpha * acc (+ beta * C when
         // beta is nonzero; C is not read otherwise).
         const bool interior = tile_inside;
+        if constexpr (CF::B_INTERLEAVE) {
+            // A lane's four blocks hold four neighbouring columns of each of
+            // its rows: 16-byte stores (and loads of C when beta is nonzero)
+            // where C allows.  Interleaved columns with 4-byte stores wrote
+            // partial cache lines and cost 6 % at square 4096; with these, the
+            // interleave measured square 4096 0.959 -> 0.948 ms, 8192 7.61 ->
+            // 7.52, 5632 2.62 -> 2.59 on MI355X (one 16-byte LDS read per k
+            // step in place of two two-float reads).
+            const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
+            if (interior && vec_c) {
+#pragma unroll
+                for (int mb = 0; mb < TM; mb++) {
+                    const int rbase = row0 + CF::a_row(wm, mb, 0) + ls * 4;
+                    float* cp = C + (int64_t)rbase * ldc + col0 + CF::b_col(wn, 0, li);
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        v4f* d = (v4f*)(cp + (int64_t)((r / 4) * 8 + (r % 4)) * ldc);
+                        v4f v;
+#pragma unroll
+                        for (int nb = 0; nb < 4; nb++) v[nb] = alpha * acc[mb][nb][r];
+                        if (read_c) {
+                            const v4f c0 = *d;
+#pragma unroll
+                            for (int nb = 0; nb < 4; nb++) v[nb] = fmaf(beta, c0[nb], v[nb]);
+                        }
+                        if constexpr (SPLITK) *d = v;
+                        else __builtin_nontemporal_store(v, d);
+                    }
+                }
+                continue;
+            }
+        }
 #pragma unroll
         for (int mb = 0; mb < TM; mb++)
 #pragma unroll
             for (int nb = 0; nb < TN; nb++) {
-                const int c = col0 + wn * TN * 32 + nb * 32 + li;
-                const int rbase = row0 + wm * TM * 32 + mb * 32 + ls * 4;
+                const int c = col0 + CF::b_col(wn, nb, li);
+                const int rbase = row0 + CF::a_row(wm, mb, 0) + ls * 4;
                 float* cp = C + (int64_t)rbase * ldc + c;
                 if (interior && !read_c) {
                     // The final C goes out with non-temporal stores (0.1-0.8 %

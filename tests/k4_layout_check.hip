@@ -45,12 +45,33 @@ void check_frags(const char* name) {
     constexpr int WAVES = IS_A ? CF::WAVES_M : CF::WAVES_N, T = IS_A ? CF::TM : CF::TN;
     for (int w = 0; w < WAVES; w++)
         for (int blk = 0; blk < T; blk++) {
-            if constexpr (KM) {
+            auto major = [&](int l) { return IS_A ? CF::a_row(w, blk, l & 31) : CF::b_col(w, blk, l & 31); };
+            if constexpr (!IS_A && CF::B_INTERLEAVE) {
+                // One ds_read_b128 per k step covers the lane's four blocks:
+                // 16-byte aligned, the four columns contiguous, 16 lanes per
+                // 256-byte bank window.
+                if (blk != 0) continue;
+                for (int t = 0; t < CF::KH; t++)
+                    for (int g = 0; g < 4; g++) {
+                        std::vector<int> slot(16, 0);
+                        for (int l = 16 * g; l < 16 * g + 16; l++) {
+                            const int k = CF::kslot(l >> 5, t);
+                            const int off = CF::b_elem(k, CF::b_col(w, 0, l & 31));
+                            CHECK(off % 16 == 0, "%s interleaved b128 misaligned", name);
+                            for (int e = 1; e < 4; e++)
+                                CHECK(CF::b_elem(k, CF::b_col(w, e, l & 31)) == off + 4 * e,
+                                      "%s interleaved b128 not contiguous", name);
+                            slot[(off / 16) % 16]++;
+                        }
+                        for (int s = 0; s < 16; s++)
+                            CHECK(slot[s] <= 1, "%s interleaved b128 bank conflict w=%d t=%d g=%d", name, w, t, g);
+                    }
+            } else if constexpr (KM) {
                 for (int q = 0; q < CF::KH / 4; q++)
                     for (int g = 0; g < 4; g++) {
                         std::vector<int> slot(16, 0);
                         for (int l = 16 * g; l < 16 * g + 16; l++) {
-                            const int mj = w * T * 32 + blk * 32 + (l & 31), k = CF::kslot(l >> 5, 4 * q);
+                            const int mj = major(l), k = CF::kslot(l >> 5, 4 * q);
                             const int off = IS_A ? CF::a_elem(mj, k) : CF::b_elem(k, mj);
                             CHECK(off % 16 == 0, "%s frag b128 misaligned", name);
                             // the 4 values of the read are k..k+3
@@ -66,7 +87,7 @@ void check_frags(const char* name) {
                 for (int t = 0; t < CF::KH; t++) {
                     std::vector<int> bank(64, 0);
                     for (int l = 0; l < 64; l++) {
-                        const int mj = w * T * 32 + blk * 32 + (l & 31), k = CF::kslot(l >> 5, t);
+                        const int mj = major(l), k = CF::kslot(l >> 5, t);
                         const int off = IS_A ? CF::a_elem(mj, k) : CF::b_elem(k, mj);
                         bank[(off / 4) % 64]++;
                     }
@@ -87,6 +108,19 @@ void check(const char* name) {
     for (int k = 0; k < CF::BK; k++) CHECK(seenK[k] == 1, "%s kslot %d", name, k);
     check_frags<CF, true>(name);
     check_frags<CF, false>(name);
+    // Each wave's accumulator blocks cover its rows and columns exactly once.
+    for (int w = 0; w < CF::WAVES_M; w++) {
+        std::vector<int> seen(CF::TM * 32, 0);
+        for (int mb = 0; mb < CF::TM; mb++)
+            for (int j = 0; j < 32; j++) seen[CF::a_row(w, mb, j) - w * CF::TM * 32]++;
+        for (int r = 0; r < CF::TM * 32; r++) CHECK(seen[r] == 1, "%s row map w=%d r=%d", name, w, r);
+    }
+    for (int w = 0; w < CF::WAVES_N; w++) {
+        std::vector<int> seen(CF::TN * 32, 0);
+        for (int nb = 0; nb < CF::TN; nb++)
+            for (int j = 0; j < 32; j++) seen[CF::b_col(w, nb, j) - w * CF::TN * 32]++;
+        for (int c = 0; c < CF::TN * 32; c++) CHECK(seen[c] == 1, "%s column map w=%d c=%d", name, w, c);
+    }
     printf("%-34s BMxBN=%3dx%-3d BK=%d threads=%4d LDS=%6d A_instr/wave=%d B_instr/wave=%d\n", name,
            CF::BM, CF::BN, CF::BK, CF::THREADS, CF::LDS_BYTES, CF::A_INSTR_PER_WAVE, CF::B_INSTR_PER_WAVE);
 }

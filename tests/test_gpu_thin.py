@@ -183,3 +183,29 @@ def test_thin_transposed_padded_ldc(case):
     assert torch.all(full[:, N:] == 555.0) and torch.all(Cbuf[M * ldc:].cpu() == 555.0), "wrote outside C"
     ref, _, _ = oracle.sgemm_ex_f64(ta, tb, 2.0, as_numpy(As), as_numpy(Bs), -1.0, as_numpy(C0))
     assert np.array_equal(full[:, :N].numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("shape", [(1, 16384, 16384), (16384, 1, 16384)], ids=["thin_m", "thin_n"])
+def test_explicit_k4_mfma_stays_on_matrix_cores(shape):
+    """SGEMM_K4_MFMA runs the matrix-core kernel even where AUTO streams the
+    product through the thin kernels: both meet the bound (integer operands:
+    both exact), and on uniform operands their results differ, as two
+    different summation orders do (both kernels are deterministic, so the
+    difference is a property of these seeds, not chance)."""
+    M, N, K = shape
+    assert rs.plan_config(M, N, K, A_ptr=1 << 40, B_ptr=1 << 40)["engine"] == "thin"
+    from tests.gpu_util import run
+    A, B = make_operands(M, N, K, "int", seed=M + 2)
+    ref, _ = oracle.sgemm_f64(as_numpy(A), as_numpy(B), bound=False)
+    for v in ("auto", "k4_mfma"):
+        note(f"[thin-vs-k4] {v} {M}x{N}x{K} int")
+        C, out = run(v, A, B)
+        assert out.guard_intact() and np.array_equal(C.astype(np.float64), ref), v
+    A, B = make_operands(M, N, K, "uniform", seed=M + 3)
+    ref, S = oracle.sgemm_f64(as_numpy(A), as_numpy(B))
+    got = {}
+    for v in ("auto", "k4_mfma"):
+        note(f"[thin-vs-k4] {v} {M}x{N}x{K} uniform")
+        got[v], _ = run(v, A, B)
+        assert check.check(got[v], ref, S, K)["ok"], v
+    assert not np.array_equal(got["auto"], got["k4_mfma"])
