@@ -6,8 +6,9 @@
 // leaves its stage, and fragment reads are spread over the LDS banks).
 //
 // Geometry: WAVES_M x WAVES_N waves per workgroup; each wave owns TM x TN
-// blocks of 32 x 32 outputs (one v_mfma_f32_32x32x2_f32 accumulator each).
-// The workgroup tile is BM x BN = (WAVES_M*TM*32) x (WAVES_N*TN*32); K is
+// blocks of 32 x 32 outputs (one v_mfma_f32_32x32x2_f32 accumulator each, or
+// with MF16 four v_mfma_f32_16x16x4_f32 accumulators of 16 x 16).  The
+// workgroup tile is BM x BN = (WAVES_M*TM*32) x (WAVES_N*TN*32); K is
 // consumed in slabs of BK.
 //
 // Each operand tile is staged in one of two layouts, after how it is stored
@@ -32,8 +33,11 @@
 // bytes.
 //
 // MFMA operand k-slots: lane L of the 32x32x2 instruction supplies A[L%32][s]
-// and B[s][L%32], s = L/32.  Slot s at step t (t < BK/2) stands for slab
-// column k = s*BK/2 + t.
+// and B[s][L%32], s = L/32; of the 16x16x4 one A[L%16][s] and B[s][L%16],
+// s = L/16.  Slot s at step t (t < KH = BK/KSLOTS) stands for slab column
+// k = s*KH + t.  With four slots the KMajor swizzle still spreads the sixteen
+// rows of a slot group over all 64 banks, and the KRows gap puts the four
+// groups' rows on disjoint quarters of the banks (16-column runs).
 //
 // Columns of a wave's accumulator blocks: block nb's column j (the lane's
 // L%32) is tile column wn*TN*32 + nb*32 + j, except with B stored K x N and
@@ -115,12 +119,22 @@ template <class T, class F> struct pick<false, T, F> { using type = F; };
 // A_KMAJOR: A stored M x K (k contiguous) rather than K x M.
 // B_KMAJOR: B stored N x K (k contiguous) rather than K x N.
 // NSTAGE: LDS stages (slabs in flight); loads run NSTAGE - 1 slabs ahead.
+// MF16: the wave's 32 x 32 blocks are each computed as four 16 x 16
+// accumulators of v_mfma_f32_16x16x4_f32 (four independent chains in place
+// of one).
 template <int WAVES_M_, int WAVES_N_, int TM_, int TN_, int BK_, bool VEC_, bool A_KMAJOR_ = true,
-          bool B_KMAJOR_ = false, int NSTAGE_ = 2>
+          bool B_KMAJOR_ = false, int NSTAGE_ = 2, bool MF16_ = false>
 struct Cfg {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_, BK = BK_;
     static constexpr bool VEC = VEC_, A_KMAJOR = A_KMAJOR_, B_KMAJOR = B_KMAJOR_;
     static constexpr int NSTAGE = NSTAGE_;
+    static constexpr bool MF16 = MF16_;
+    // Accumulator block edge, blocks per wave along M and N, k-slots of one
+    // instruction (lane groups), and accumulator registers per lane.
+    static constexpr int BLK = MF16 ? 16 : 32;
+    static constexpr int MB = TM * 32 / BLK, NB = TN * 32 / BLK;
+    static constexpr int KSLOTS = 64 / BLK;
+    static constexpr int NREG = BLK * BLK / 64;
     static constexpr int NWAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * NWAVES;
     static constexpr int BM = WAVES_M * TM * 32, BN = WAVES_N * TN * 32;
@@ -131,19 +145,25 @@ struct Cfg {
     static constexpr int LDS_BYTES = NSTAGE * STAGE;
     static constexpr int A_INSTR_PER_WAVE = LA::INSTR / NWAVES;
     static constexpr int B_INSTR_PER_WAVE = LB::INSTR / NWAVES;
-    static constexpr int KH = BK / 2;       // MFMA steps per slab
+    static constexpr int KH = BK / KSLOTS;  // MFMA steps per slab
     static_assert(BK == 16 || BK == 32, "slab depth");
     static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stages");
     static_assert(LA::INSTR % NWAVES == 0 && LB::INSTR % NWAVES == 0, "loads split evenly over waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 
-    static constexpr bool B_INTERLEAVE = !B_KMAJOR && TN == 4;
+    static constexpr bool B_INTERLEAVE = !B_KMAJOR && TN == 4 && !MF16;
     // Slab column that k-slot s stands for at MFMA step t.
     __host__ __device__ static constexpr int kslot(int s, int t) { return s * KH + t; }
-    // Tile row and column of a wave's accumulator blocks (lane index j = L%32).
-    __host__ __device__ static constexpr int a_row(int wm, int mb, int j) { return wm * TM * 32 + mb * 32 + j; }
+    // Tile row and column of a wave's accumulator blocks (lane index
+    // j = L % BLK).
+    __host__ __device__ static constexpr int a_row(int wm, int mb, int j) { return wm * TM * 32 + mb * BLK + j; }
     __host__ __device__ static constexpr int b_col(int wn, int nb, int j) {
-        return B_INTERLEAVE ? wn * TN * 32 + 4 * j + nb : wn * TN * 32 + nb * 32 + j;
+        return B_INTERLEAVE ? wn * TN * 32 + 4 * j + nb : wn * TN * 32 + nb * BLK + j;
+    }
+    // Row within its block of accumulator register r of a lane in k-slot
+    // group s = L / BLK (its column is L % BLK).
+    __host__ __device__ static constexpr int acc_row(int s, int r) {
+        return MF16 ? 4 * s + r : 8 * (r / 4) + 4 * s + r % 4;
     }
     // Stage bytes of A(m, k) and B(k, n) for tile-local m, n, k.
     __host__ __device__ static constexpr int a_elem(int m, int k) {

@@ -6,7 +6,10 @@
 // last step of the ladder.  On CDNA4 one v_mfma_f32_32x32x2_f32 multiplies a
 // 32 x 2 slice of A by a 2 x 32 slice of B into a 32 x 32 float accumulator
 // held across the wave's 64 lanes (16 registers per lane), at the same FP32
-// rate as the vector units' peak but from two operand registers per lane.
+// rate as the vector units' peak but from two operand registers per lane;
+// v_mfma_f32_16x16x4_f32 does a 16 x 4 by 4 x 16 product into a 16 x 16
+// accumulator (4 registers per lane) at the same rate, and some tile
+// configurations build each 32 x 32 block from four of those.
 //
 // Structure (geometry and LDS layouts in k4_layout.h):
 //  * a workgroup owns a BM x BN tile of C; each wave TM x TN accumulators;
@@ -106,7 +109,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         int tiles_n, int tiles, int kchunk) {
     // 32-bit sizes: the host routes shapes whose sizes, leading dimensions
     // or slab offsets do not fit (k4_supports) to the 64-bit kernel.
-    constexpr int TM = CF::TM, TN = CF::TN, KH = CF::KH;
+    // MB x NB accumulator blocks per wave (32 x 32, or 16 x 16 with MF16).
+    constexpr int MB = CF::MB, NB = CF::NB, KH = CF::KH, NREG = CF::NREG;
+    using Acc = typename std::conditional<CF::MF16, v4f, v16f>::type;
     constexpr int WG_WAVES = CF::NWAVES;  // waves of one K group
     // The K groups' partial tiles, rows padded to BN + 8 floats (WK > 1).
     constexpr int RLD = CF::BN + 8;
@@ -133,7 +138,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
     const int kg = WK > 1 ? wave_all / WG_WAVES : 0;       // K group
     const int wave = WK > 1 ? wave_all % WG_WAVES : wave_all;  // wave within the group
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
-    const int li = lane & 31, ls = lane >> 5;
+    const int li = CF::MF16 ? lane & 15 : lane & 31, ls = CF::MF16 ? lane >> 4 : lane >> 5;
 
     const bool direct = XCD_REMAP && (int)gridDim.x == tiles;
     for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
@@ -209,13 +214,13 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         };
         const bool tile_inside = row0 + CF::BM <= M && col0 + CF::BN <= N;
 
-        v16f acc[TM][TN];
+        Acc acc[MB][NB];
 #pragma unroll
-        for (int mb = 0; mb < TM; mb++)
+        for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int nb = 0; nb < TN; nb++)
+            for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.0f;
+                for (int r = 0; r < NREG; r++) acc[mb][nb][r] = 0.0f;
 
         // The group's s-th slab (K slab s * WK + kg) lives in stage s % NS;
         // loads run NS - 1 slabs ahead.  Every wave issues PER load
@@ -250,9 +255,10 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             // Fragments are read and consumed in NH parts of KH / NH steps;
             // with NH = 2 only half of them are live at a time.
             constexpr int NH = SPLIT ? 2 : 1, KP = KH / NH;
-            auto read_frags = [&](int h, float (&af)[TM][KP], float (&bf)[TN][KP]) {
+            static_assert(!(CF::A_KMAJOR || CF::B_KMAJOR) || KP % 4 == 0, "16-byte fragment reads");
+            auto read_frags = [&](int h, float (&af)[MB][KP], float (&bf)[NB][KP]) {
 #pragma unroll
-                for (int mb = 0; mb < TM; mb++) {
+                for (int mb = 0; mb < MB; mb++) {
                     const int row = CF::a_row(wm, mb, li);
                     if constexpr (CF::A_KMAJOR) {
 #pragma unroll
@@ -273,11 +279,11 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                     for (int u = 0; u < KP; u++) {
                         const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), CF::b_col(wn, 0, li)));
 #pragma unroll
-                        for (int nb = 0; nb < TN; nb++) bf[nb][u] = v[nb];
+                        for (int nb = 0; nb < NB; nb++) bf[nb][u] = v[nb];
                     }
                 } else {
 #pragma unroll
-                    for (int nb = 0; nb < TN; nb++) {
+                    for (int nb = 0; nb < NB; nb++) {
                         const int col = CF::b_col(wn, nb, li);
                         if constexpr (CF::B_KMAJOR) {
 #pragma unroll
@@ -294,18 +300,23 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                     }
                 }
             };
-            auto mfmas = [&](const float (&af)[TM][KP], const float (&bf)[TN][KP]) {
+            auto mfmas = [&](const float (&af)[MB][KP], const float (&bf)[NB][KP]) {
 #pragma unroll
                 for (int u = 0; u < KP; u++)
 #pragma unroll
-                    for (int mb = 0; mb < TM; mb++)
+                    for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-                        for (int nb = 0; nb < TN; nb++)
-                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb][u], bf[nb][u],
-                                                                               acc[mb][nb], 0, 0, 0);
+                        for (int nb = 0; nb < NB; nb++) {
+                            if constexpr (CF::MF16)
+                                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mb][u], bf[nb][u],
+                                                                                   acc[mb][nb], 0, 0, 0);
+                            else
+                                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[mb][u], bf[nb][u],
+                                                                                   acc[mb][nb], 0, 0, 0);
+                        }
             };
             if (WK == 1 || s < nk) {
-                float af[TM][KP], bf[TN][KP];
+                float af[MB][KP], bf[NB][KP];
                 read_frags(0, af, bf);
                 // The slab NS - 1 ahead goes to the stage read in the
                 // previous iteration (every wave has passed that iteration's
@@ -334,9 +345,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             // and barrier below, which would expose the load latency; tie
             // the accumulators to this point.
 #pragma unroll
-            for (int mb = 0; mb < TM; mb++)
+            for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-                for (int nb = 0; nb < TN; nb++) asm volatile("" : "+a"(acc[mb][nb]));
+                for (int nb = 0; nb < NB; nb++) asm volatile("" : "+a"(acc[mb][nb]));
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             // Slab s + 1 landed: the slabs after it may stay in flight.
             const int newer = nk - 2 - s < NS - 2 ? nk - 2 - s : NS - 2;
@@ -368,12 +379,13 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                           "whole 16-byte chunks per lane");
             float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-            for (int mb = 0; mb < TM; mb++)
+            for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-                for (int nb = 0; nb < TN; nb++)
+                for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int row = CF::a_row(wm, mb, 0) + (r / 4) * 8 + ls * 4 + r % 4;
+                    for (int r = 0; r < NREG; r++) {
+                        const int row = CF::MF16 ? CF::a_row(wm, mb, 0) + ls * 4 + r
+                                                 : CF::a_row(wm, mb, 0) + (r / 4) * 8 + ls * 4 + r % 4;
                         const int col = CF::b_col(wn, nb, li);
                         red[(kg * CF::BM + row) * RLD + col] = acc[mb][nb][r];
                     }
@@ -413,9 +425,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             continue;
         }
 
-        // Accumulator register r of lane L holds row 8*(r/4) + 4*(L/32) + r%4,
-        // column L%32 of its 32 x 32 block.  C = alpha * acc (+ beta * C when
-        // beta is nonzero; C is not read otherwise).
+        // Accumulator register r of lane L holds row acc_row(L / BLK, r),
+        // column L % BLK of its block.  C = alpha * acc (+ beta * C when beta
+        // is nonzero; C is not read otherwise).
         const bool interior = tile_inside;
         if constexpr (CF::B_INTERLEAVE) {
             // A lane's four blocks hold four neighbouring columns of each of
@@ -428,7 +440,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
             if (interior && vec_c) {
 #pragma unroll
-                for (int mb = 0; mb < TM; mb++) {
+                for (int mb = 0; mb < MB; mb++) {
                     const int rbase = row0 + CF::a_row(wm, mb, 0) + ls * 4;
                     float* cp = C + (int64_t)rbase * ldc + col0 + CF::b_col(wn, 0, li);
 #pragma unroll
@@ -450,26 +462,26 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             }
         }
 #pragma unroll
-        for (int mb = 0; mb < TM; mb++)
+        for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-            for (int nb = 0; nb < TN; nb++) {
+            for (int nb = 0; nb < NB; nb++) {
                 const int c = col0 + CF::b_col(wn, nb, li);
-                const int rbase = row0 + CF::a_row(wm, mb, 0) + ls * 4;
+                const int rbase = row0 + CF::a_row(wm, mb, 0) + CF::acc_row(ls, 0);
                 float* cp = C + (int64_t)rbase * ldc + c;
                 if (interior && !read_c) {
                     // The final C goes out with non-temporal stores (0.1-0.8 %
                     // faster on unsplit products); split partial tiles, which
                     // the reduction reads right back, keep the default policy.
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        float* d = cp + (int64_t)((r / 4) * 8 + (r % 4)) * ldc;
+                    for (int r = 0; r < NREG; r++) {
+                        float* d = cp + (int64_t)(CF::acc_row(0, r)) * ldc;
                         if constexpr (SPLITK) *d = alpha * acc[mb][nb][r];
                         else __builtin_nontemporal_store(alpha * acc[mb][nb][r], d);
                     }
                 } else if (c < N) {
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int dr = (r / 4) * 8 + (r % 4);
+                    for (int r = 0; r < NREG; r++) {
+                        const int dr = CF::acc_row(0, r);
                         if (rbase + dr < M) {
                             float v = alpha * acc[mb][nb][r];
                             if (read_c) v = fmaf(beta, cp[(int64_t)dr * ldc], v);
@@ -591,28 +603,28 @@ hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float
 // 55,296 B of LDS (52,224 B with A stored M x K), so three workgroups would
 // need 165,888 B, more than the CU's 160 KiB, and the target drops to 2.
 template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2,
-          int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC, int UNCHK = 2>
+          int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC, int UNCHK = 2, bool MF16 = false>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,
                             float* ws = nullptr) {
     using k4::Cfg;
     if constexpr (CAN_SPLIT) {
         if (splits > 1) {
             if (!g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
             if (!g.trans_a && g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
             if (g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC_TN, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
-            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
         }
     }
     if (!g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS>, OCC, SPLIT, WK, false, UNCHK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, false, UNCHK>(g, s);
     if (!g.trans_a && g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS>, OCC, SPLIT, WK, false, UNCHK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK>(g, s);
     if (g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS>, OCC_TN, SPLIT, WK, false, UNCHK>(g, s);
-    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS>, OCC, SPLIT, WK, false, UNCHK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, false, UNCHK>(g, s);
+    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK>(g, s);
 }
 
 // Largest byte offset a slab reaches from its base, per operand orientation.
@@ -658,13 +670,23 @@ hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s) {
     return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, false>, 2, true, 1, true>(g, s);
 }
 
+// The 128 x 128 and 64 x 64 tiles with 16-byte loads run on the 16 x 16 x 4
+// instruction: each 32 x 32 block becomes four independent accumulator
+// chains.  Measured on MI355X against the 32 x 32 x 2 kernel (integer
+// operands bit-identical in all four orientations): 128 x 128 tiles square
+// 6144 3.306 -> 3.256 ms, 7168^2 x 1024 0.863 -> 0.846; 64 x 64 tiles
+// 3001 x 4099 x 2047 428 -> 421 us, square 3072 450 -> 438, 1536 x 1024 x
+// 1024 36.0 -> 34.8, 1280^3 47.3 -> 46.8.  It does not help the K-group
+// tiles (square 1024 21.80 against 21.77 us, 1024^2 x 4096 73.4 against
+// 73.2), costs 32 x 32 tiles 3-6 % (640^3 9.16 -> 9.69 us) and spills
+// registers in the 128 x 256 tile (square 4096 0.942 -> 0.960 ms).
 hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4, false, 2, 1, false>(g, s);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 2, 2, 16, true, 4, false, 2, 1, false, 4, 2, true>(g, s);
     return launch_k4_orient<2, 2, 2, 2, 16, false, 3, false, 2, 1, false>(g, s);
 }
 
 hipError_t launch_k4_t64(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true>(g, s, splits, kchunk, ws);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true, 2, 1, true, 4, 2, true>(g, s, splits, kchunk, ws);
     return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, splits, kchunk, ws);
 }
 

@@ -36,16 +36,19 @@ void check_operand(const char* name, int major_extent) {
     for (size_t i = 0; i < seen.size(); i++) CHECK(seen[i] == 1, "%s element %zu loaded %d times", name, i, seen[i]);
 }
 
-// Fragment reads of one operand by one wave: lanes (li, ls) read
-// (major = base + li, k = kslot(ls, t)).  KMajor: ds_read_b128 per 4 steps,
-// 16 lanes per 256-byte bank window; KRows: ds_read_b32, 64 lanes over 64 banks.
+// Fragment reads of one operand by one wave: lane l reads
+// (major = base + l % BLK, k = kslot(l / BLK, t)).  KMajor: ds_read_b128 per
+// 4 steps, 16 lanes per 256-byte bank window; KRows: ds_read_b32, 64 lanes
+// over 64 banks.
 template <class CF, bool IS_A>
 void check_frags(const char* name) {
     constexpr bool KM = IS_A ? CF::A_KMAJOR : CF::B_KMAJOR;
-    constexpr int WAVES = IS_A ? CF::WAVES_M : CF::WAVES_N, T = IS_A ? CF::TM : CF::TN;
+    constexpr int WAVES = IS_A ? CF::WAVES_M : CF::WAVES_N, T = IS_A ? CF::MB : CF::NB;
     for (int w = 0; w < WAVES; w++)
         for (int blk = 0; blk < T; blk++) {
-            auto major = [&](int l) { return IS_A ? CF::a_row(w, blk, l & 31) : CF::b_col(w, blk, l & 31); };
+            auto major = [&](int l) {
+                return IS_A ? CF::a_row(w, blk, l % CF::BLK) : CF::b_col(w, blk, l % CF::BLK);
+            };
             if constexpr (!IS_A && CF::B_INTERLEAVE) {
                 // One ds_read_b128 per k step covers the lane's four blocks:
                 // 16-byte aligned, the four columns contiguous, 16 lanes per
@@ -71,7 +74,7 @@ void check_frags(const char* name) {
                     for (int g = 0; g < 4; g++) {
                         std::vector<int> slot(16, 0);
                         for (int l = 16 * g; l < 16 * g + 16; l++) {
-                            const int mj = major(l), k = CF::kslot(l >> 5, 4 * q);
+                            const int mj = major(l), k = CF::kslot(l / CF::BLK, 4 * q);
                             const int off = IS_A ? CF::a_elem(mj, k) : CF::b_elem(k, mj);
                             CHECK(off % 16 == 0, "%s frag b128 misaligned", name);
                             // the 4 values of the read are k..k+3
@@ -87,7 +90,7 @@ void check_frags(const char* name) {
                 for (int t = 0; t < CF::KH; t++) {
                     std::vector<int> bank(64, 0);
                     for (int l = 0; l < 64; l++) {
-                        const int mj = major(l), k = CF::kslot(l >> 5, t);
+                        const int mj = major(l), k = CF::kslot(l / CF::BLK, t);
                         const int off = IS_A ? CF::a_elem(mj, k) : CF::b_elem(k, mj);
                         bank[(off / 4) % 64]++;
                     }
@@ -99,30 +102,44 @@ void check_frags(const char* name) {
 
 template <class CF>
 void check(const char* name) {
+    const int failures_before = failures;
     check_operand<typename CF::LA>(name, CF::BM);
     check_operand<typename CF::LB>(name, CF::BN);
     // A and B stages do not overlap; both stages fit the allocation.
     CHECK(CF::B_BASE >= CF::LA::STAGE && CF::B_BASE + CF::LB::STAGE == CF::STAGE, "%s stage split", name);
     std::vector<int> seenK(CF::BK, 0);
-    for (int s = 0; s < 2; s++) for (int t = 0; t < CF::KH; t++) seenK[CF::kslot(s, t)]++;
+    for (int s = 0; s < CF::KSLOTS; s++) for (int t = 0; t < CF::KH; t++) seenK[CF::kslot(s, t)]++;
     for (int k = 0; k < CF::BK; k++) CHECK(seenK[k] == 1, "%s kslot %d", name, k);
     check_frags<CF, true>(name);
     check_frags<CF, false>(name);
     // Each wave's accumulator blocks cover its rows and columns exactly once.
     for (int w = 0; w < CF::WAVES_M; w++) {
         std::vector<int> seen(CF::TM * 32, 0);
-        for (int mb = 0; mb < CF::TM; mb++)
-            for (int j = 0; j < 32; j++) seen[CF::a_row(w, mb, j) - w * CF::TM * 32]++;
+        for (int mb = 0; mb < CF::MB; mb++)
+            for (int j = 0; j < CF::BLK; j++) seen[CF::a_row(w, mb, j) - w * CF::TM * 32]++;
         for (int r = 0; r < CF::TM * 32; r++) CHECK(seen[r] == 1, "%s row map w=%d r=%d", name, w, r);
     }
     for (int w = 0; w < CF::WAVES_N; w++) {
         std::vector<int> seen(CF::TN * 32, 0);
-        for (int nb = 0; nb < CF::TN; nb++)
-            for (int j = 0; j < 32; j++) seen[CF::b_col(w, nb, j) - w * CF::TN * 32]++;
+        for (int nb = 0; nb < CF::NB; nb++)
+            for (int j = 0; j < CF::BLK; j++) seen[CF::b_col(w, nb, j) - w * CF::TN * 32]++;
         for (int c = 0; c < CF::TN * 32; c++) CHECK(seen[c] == 1, "%s column map w=%d c=%d", name, w, c);
     }
-    printf("%-34s BMxBN=%3dx%-3d BK=%d threads=%4d LDS=%6d A_instr/wave=%d B_instr/wave=%d\n", name,
-           CF::BM, CF::BN, CF::BK, CF::THREADS, CF::LDS_BYTES, CF::A_INSTR_PER_WAVE, CF::B_INSTR_PER_WAVE);
+    // The accumulator registers of a block's 64 lanes (row acc_row(l / BLK,
+    // r), column l % BLK) hold each of its BLK x BLK outputs once.
+    {
+        std::vector<int> seen(CF::BLK * CF::BLK, 0);
+        for (int l = 0; l < 64; l++)
+            for (int r = 0; r < CF::NREG; r++) {
+                const int row = CF::acc_row(l / CF::BLK, r);
+                CHECK(row >= 0 && row < CF::BLK, "%s accumulator row %d", name, row);
+                if (row >= 0 && row < CF::BLK) seen[row * CF::BLK + l % CF::BLK]++;
+            }
+        for (int i = 0; i < CF::BLK * CF::BLK; i++) CHECK(seen[i] == 1, "%s accumulator element %d", name, i);
+    }
+    printf("%-39s BMxBN=%3dx%-3d BK=%d threads=%4d LDS=%6d A_instr/wave=%d B_instr/wave=%d%s\n", name,
+           CF::BM, CF::BN, CF::BK, CF::THREADS, CF::LDS_BYTES, CF::A_INSTR_PER_WAVE, CF::B_INSTR_PER_WAVE,
+           failures > failures_before ? "  FAILED" : "");
 }
 
 #define CFG1(wm, wn, tm, tn, bk, v, ak, bk2) \
@@ -132,6 +149,15 @@ void check(const char* name) {
     CFG1(wm, wn, tm, tn, bk, true, true, true) CFG1(wm, wn, tm, tn, bk, false, true, true)       \
     CFG1(wm, wn, tm, tn, bk, true, false, false) CFG1(wm, wn, tm, tn, bk, false, false, false)   \
     CFG1(wm, wn, tm, tn, bk, true, false, true) CFG1(wm, wn, tm, tn, bk, false, false, true)
+
+// The same with the 16 x 16 x 4 instruction (four k-slot lane groups).
+#define CFG1M(wm, wn, tm, tn, bk, v, ak, bk2) \
+    check<Cfg<wm, wn, tm, tn, bk, v, ak, bk2, 2, true>>("Cfg<" #wm "," #wn "," #tm "," #tn "," #bk "," #v "," #ak "," #bk2 ",MF16>");
+#define CFGM(wm, wn, tm, tn, bk)                                                                    \
+    CFG1M(wm, wn, tm, tn, bk, true, true, false) CFG1M(wm, wn, tm, tn, bk, false, true, false)     \
+    CFG1M(wm, wn, tm, tn, bk, true, true, true) CFG1M(wm, wn, tm, tn, bk, false, true, true)       \
+    CFG1M(wm, wn, tm, tn, bk, true, false, false) CFG1M(wm, wn, tm, tn, bk, false, false, false)   \
+    CFG1M(wm, wn, tm, tn, bk, true, false, true) CFG1M(wm, wn, tm, tn, bk, false, false, true)
 
 int main() {
     CFG(2, 2, 2, 2, 16)
@@ -150,6 +176,14 @@ int main() {
     CFG(4, 2, 1, 2, 32)
     CFG(2, 2, 2, 4, 16)
     CFG(1, 1, 1, 1, 32)
+    CFGM(2, 2, 2, 2, 16)
+    CFGM(2, 2, 1, 1, 16)
+    CFGM(2, 2, 1, 1, 32)
+    // (32 x 32 tiles with slabs of 16 are left out: there the 32-column
+    // KRows image puts k-slot groups 0 and 1 on the same banks, a two-way
+    // conflict on every b32 read; no launcher builds that configuration.)
+    CFGM(1, 1, 1, 1, 32)
+    CFGM(2, 2, 2, 4, 16)
     printf("failures: %d\n", failures);
     return failures ? 1 : 0;
 }
