@@ -626,11 +626,11 @@ hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, 
 // K split into `splits` chunks of kchunk (a multiple of BK; every chunk
 // nonempty): partial products into ws (splits slabs of M rows of
 // split_ld(N) floats), then the reduction into C.
-template <class CF, int OCC, bool SPLIT = false, int WK = 1, int UNCHK = 2>
+template <class CF, int OCC, bool SPLIT = false, int WK = 1, int UNCHK = 2, bool PIPE = false>
 hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
     const int64_t ldw = split_ld(g.N);
-    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true, WK, false, UNCHK>), dim3(grid_for(tiles), splits),
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true, WK, false, UNCHK, PIPE>), dim3(grid_for(tiles), splits),
                        dim3(CF::THREADS * WK), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, ws, ldw,
                        1.0f, 0.0f, (int)tm, (int)tn, (int)tiles, kchunk);
@@ -647,28 +647,29 @@ hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float
 // 55,296 B of LDS (52,224 B with A stored M x K), so three workgroups would
 // need 165,888 B, more than the CU's 160 KiB, and the target drops to 2.
 template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2,
-          int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC, int UNCHK = 2, bool MF16 = false>
+          int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC, int UNCHK = 2, bool MF16 = false,
+          bool PIPE = false>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,
                             float* ws = nullptr) {
     using k4::Cfg;
     if constexpr (CAN_SPLIT) {
         if (splits > 1) {
             if (!g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
             if (!g.trans_a && g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
             if (g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
-            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, UNCHK>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
         }
     }
     if (!g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, false, UNCHK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE>(g, s);
     if (!g.trans_a && g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE>(g, s);
     if (g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, false, UNCHK>(g, s);
-    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, false, UNCHK, PIPE>(g, s);
+    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE>(g, s);
 }
 
 // Largest byte offset a slab reaches from its base, per operand orientation.
@@ -729,6 +730,8 @@ hipError_t launch_k4_tile128(const GemmArgs& g, hipStream_t s) {
     return launch_k4_orient<2, 2, 2, 2, 16, false, 3, false, 2, 1, false>(g, s);
 }
 
+// The pipelined slab (PIPE) measured slower here: 3001 x 4099 x 2047 423 ->
+// 444 us, square 3072 440 -> 443.
 hipError_t launch_k4_t64(const GemmArgs& g, hipStream_t s, int splits, int kchunk, float* ws) {
     if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true, 2, 1, true, 4, 2, true>(g, s, splits, kchunk, ws);
     return launch_k4_orient<2, 2, 1, 1, 16, false, 8>(g, s, splits, kchunk, ws);
@@ -748,21 +751,26 @@ hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int k
     // -> 31.1, 512 x 256 x 8192 29.9 -> 28.5); alone on a CU with long
     // shares the extra barriers cost more (64^2 x 65536 22.8 -> 25.3), and
     // 64 x 64 tiles lose 5-15 % with it.
+    // Both take the pipelined slab (PIPE): square 256 4.58 -> 4.37 us, 512
+    // 6.50 -> 6.02, 640 9.27 -> 8.73, 768 x 1024 x 1024 17.6 -> 16.0,
+    // 128^2 x 4096 9.10 -> 8.94.
     if (vec_ok(g)) {
         const int64_t share = (splits > 1 ? kchunk : g.K) / 4;
         const int64_t wgs = ceil_div(g.M, 32) * ceil_div(g.N, 32) * (splits > 1 ? splits : 1);
         if (share <= 256 || wgs >= 2 * 256)
-            return launch_k4_orient<1, 1, 1, 1, 16, true, 3, true, 3, 4, true, 2>(g, s, splits, kchunk, ws);
-        return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4>(g, s, splits, kchunk, ws);
+            return launch_k4_orient<1, 1, 1, 1, 16, true, 3, true, 3, 4, true, 2, 2, false, true>(g, s, splits, kchunk, ws);
+        return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4, true, 2, 2, false, true>(g, s, splits, kchunk, ws);
     }
     return launch_k4_orient<1, 1, 1, 1, 16, false, 4, false, 2, 4>(g, s, splits, kchunk, ws);
 }
 
 // 16-byte loads only (the plan never picks it otherwise: with 4-byte loads
-// 64 x 64 tiles with K groups measured slower than 32 x 32 ones).
+// 64 x 64 tiles with K groups measured slower than 32 x 32 ones).  The
+// pipelined slab (PIPE): square 1024 22.2 -> 21.0 us, 1024^2 x 4096 73.7 ->
+// 69.1, 896^3 19.7 -> 19.0.
 hipError_t launch_k4_t64_wk4(const GemmArgs& g, hipStream_t s, int splits, int kchunk,
                                     float* ws) {
-    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true, 2, 4>(g, s, splits, kchunk, ws);
+    if (vec_ok(g)) return launch_k4_orient<2, 2, 1, 1, 32, true, 4, true, 2, 4, true, 4, 2, false, true>(g, s, splits, kchunk, ws);
     return launch_k4_t32_wk4(g, s, splits, kchunk, ws);
 }
 
