@@ -104,8 +104,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 // PIPE (with SPLIT and UNCHK = 2): in that unchecked loop, the second half's
 // fragment reads and the next slab's loads are spread among the first
 // MFMAs instead of waiting behind them.
+// NOSYNC (K groups of one wave): no barrier per slab.  Such a wave loads
+// every element of its group's stages itself and reads only those, so its
+// own wait for its loads orders them before its reads, and program order
+// (each read consumed before the loads NS - 1 slabs later are issued)
+// orders the reads before the next loads into the same stage; the groups
+// then run at their own pace until the reduction, which waits for all.
 template <class CF, int OCC, int GM = GROUP_M, bool XCD_REMAP = true, bool SPLIT = false,
-          bool SPLITK = false, int WK = 1, bool PRIO = false, int UNCHK = 2, bool PIPE = false>
+          bool SPLITK = false, int WK = 1, bool PRIO = false, int UNCHK = 2, bool PIPE = false,
+          bool NOSYNC = false>
 __global__ void __launch_bounds__(CF::THREADS * WK) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* __restrict__ B,
         int ldb, float* __restrict__ C, int64_t ldc, float alpha, float beta, int tiles_m,
@@ -250,7 +257,8 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             const int newer = nk - 1 < NS - 2 ? nk - 1 : NS - 2;
             wait_vm_batches<PER, NS - 2>(newer > 0 ? newer : 0);
         }
-        __syncthreads();
+        static_assert(!NOSYNC || CF::NWAVES == 1, "a K group of several waves shares its stages");
+        if constexpr (!NOSYNC) __syncthreads();
         // One slab: its MFMAs, and the loads of the slab NS - 1 ahead
         // (checked or not, after CHECK).
         // WHOLE: the slab NS - 1 ahead exists and is whole (the unchecked loop).
@@ -395,7 +403,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             // Slab s + 1 landed: the slabs after it may stay in flight.
             const int newer = nk - 2 - s < NS - 2 ? nk - 2 - s : NS - 2;
             wait_vm_batches<PER, NS - 2>(newer > 0 ? newer : 0);
-            __syncthreads();
+            if constexpr (!NOSYNC) __syncthreads();
         };
         // Iterations whose prefetch target is a whole slab of a tile inside
         // C skip the checks; every wave runs `iters` iterations (one barrier
@@ -409,7 +417,8 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
 
         const bool read_c = beta != 0.0f;
         if constexpr (WK > 1) {
-            // Every stage is free after the loop's last barrier.  Each K group
+            // Every stage is free after the loop's last barrier (with NOSYNC,
+            // after the one below).  Each K group
             // leaves its partial tile in LDS (a row of BN floats plus 8, so
             // the two halves of a wave's accumulator writes, four rows apart,
             // fall on disjoint banks); then every lane of the workgroup adds
@@ -420,6 +429,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             constexpr int PER_LANE = CF::BM * CF::BN / (CF::THREADS * WK);
             static_assert(PER_LANE % 4 == 0 && PER_LANE * CF::THREADS * WK == CF::BM * CF::BN,
                           "whole 16-byte chunks per lane");
+            if constexpr (NOSYNC) __syncthreads();  // every group past its last slab
             float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
             for (int mb = 0; mb < MB; mb++)
@@ -537,10 +547,10 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
 }
 
 template <class CF, int OCC, bool SPLIT = false, int WK = 1, bool PRIO = false, int UNCHK = 2,
-          bool PIPE = false>
+          bool PIPE = false, bool NOSYNC = false>
 hipError_t launch_k4_cfg(const GemmArgs& g, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
-    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, false, WK, PRIO, UNCHK, PIPE>), dim3(grid_for(tiles)),
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, false, WK, PRIO, UNCHK, PIPE, NOSYNC>), dim3(grid_for(tiles)),
                        dim3(CF::THREADS * WK), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, g.C, g.ldc,
                        g.alpha, g.beta, (int)tm, (int)tn, (int)tiles, 0);
@@ -626,11 +636,12 @@ hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* ws, 
 // K split into `splits` chunks of kchunk (a multiple of BK; every chunk
 // nonempty): partial products into ws (splits slabs of M rows of
 // split_ld(N) floats), then the reduction into C.
-template <class CF, int OCC, bool SPLIT = false, int WK = 1, int UNCHK = 2, bool PIPE = false>
+template <class CF, int OCC, bool SPLIT = false, int WK = 1, int UNCHK = 2, bool PIPE = false,
+          bool NOSYNC = false>
 hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float* ws, hipStream_t s) {
     const int64_t tm = ceil_div(g.M, CF::BM), tn = ceil_div(g.N, CF::BN), tiles = tm * tn;
     const int64_t ldw = split_ld(g.N);
-    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true, WK, false, UNCHK, PIPE>), dim3(grid_for(tiles), splits),
+    hipLaunchKernelGGL((k4_mfma<CF, OCC, GROUP_M, true, SPLIT, true, WK, false, UNCHK, PIPE, NOSYNC>), dim3(grid_for(tiles), splits),
                        dim3(CF::THREADS * WK), 0, s,
                        (int)g.M, (int)g.N, (int)g.K, g.A, (int)g.lda, g.B, (int)g.ldb, ws, ldw,
                        1.0f, 0.0f, (int)tm, (int)tn, (int)tiles, kchunk);
@@ -648,28 +659,28 @@ hipError_t launch_k4_cfg_splitk(const GemmArgs& g, int splits, int kchunk, float
 // need 165,888 B, more than the CU's 160 KiB, and the target drops to 2.
 template <int WM, int WN, int TM, int TN, int BK, bool V, int OCC, bool SPLIT = false, int NS = 2,
           int WK = 1, bool CAN_SPLIT = true, int OCC_TN = OCC, int UNCHK = 2, bool MF16 = false,
-          bool PIPE = false>
+          bool PIPE = false, bool NOSYNC = false>
 hipError_t launch_k4_orient(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0,
                             float* ws = nullptr) {
     using k4::Cfg;
     if constexpr (CAN_SPLIT) {
         if (splits > 1) {
             if (!g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE, NOSYNC>(g, splits, kchunk, ws, s);
             if (!g.trans_a && g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE, NOSYNC>(g, splits, kchunk, ws, s);
             if (g.trans_a && !g.trans_b)
-                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
-            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE>(g, splits, kchunk, ws, s);
+                return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, UNCHK, PIPE, NOSYNC>(g, splits, kchunk, ws, s);
+            return launch_k4_cfg_splitk<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, UNCHK, PIPE, NOSYNC>(g, splits, kchunk, ws, s);
         }
     }
     if (!g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, false, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE, NOSYNC>(g, s);
     if (!g.trans_a && g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, true, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE, NOSYNC>(g, s);
     if (g.trans_a && !g.trans_b)
-        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, false, UNCHK, PIPE>(g, s);
-    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE>(g, s);
+        return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, false, NS, MF16>, OCC_TN, SPLIT, WK, false, UNCHK, PIPE, NOSYNC>(g, s);
+    return launch_k4_cfg<Cfg<WM, WN, TM, TN, BK, V, false, true, NS, MF16>, OCC, SPLIT, WK, false, UNCHK, PIPE, NOSYNC>(g, s);
 }
 
 // Largest byte offset a slab reaches from its base, per operand orientation.
@@ -753,15 +764,24 @@ hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int k
     // 64 x 64 tiles lose 5-15 % with it.
     // Both take the pipelined slab (PIPE): square 256 4.58 -> 4.37 us, 512
     // 6.50 -> 6.02, 640 9.27 -> 8.73, 768 x 1024 x 1024 17.6 -> 16.0,
-    // 128^2 x 4096 9.10 -> 8.94.
+    // 128^2 x 4096 9.10 -> 8.94.  And no barrier per slab (NOSYNC), except
+    // with slabs of 16 and long shares: square 256 4.41 -> 4.18, 512 5.82 ->
+    // 5.63, 640 8.72 -> 8.43, 256^2 x 4096 12.6 -> 12.2, 64^2 x 65536 23.1 ->
+    // 20.9; with slabs of 16 and shares of 512 it cost 256^2 x 16384 7 %
+    // (27.0 -> 28.8 us; groups that drift apart no longer share the 128-byte
+    // lines of A that their 64-byte slab rows split).  4-byte loads:
+    // NOSYNC too (255^3 6.46 -> 6.27 us, 300 x 1000 x 901 19.3 -> 18.1,
+    // 1023 x 1027 x 1024 36.4 -> 35.3, 700 x 901 x 1500 35.6 -> 33.5).
     if (vec_ok(g)) {
         const int64_t share = (splits > 1 ? kchunk : g.K) / 4;
         const int64_t wgs = ceil_div(g.M, 32) * ceil_div(g.N, 32) * (splits > 1 ? splits : 1);
-        if (share <= 256 || wgs >= 2 * 256)
+        if (share <= 256)
+            return launch_k4_orient<1, 1, 1, 1, 16, true, 3, true, 3, 4, true, 2, 2, false, true, true>(g, s, splits, kchunk, ws);
+        if (wgs >= 2 * 256)
             return launch_k4_orient<1, 1, 1, 1, 16, true, 3, true, 3, 4, true, 2, 2, false, true>(g, s, splits, kchunk, ws);
-        return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4, true, 2, 2, false, true>(g, s, splits, kchunk, ws);
+        return launch_k4_orient<1, 1, 1, 1, 32, true, 2, true, 2, 4, true, 2, 2, false, true, true>(g, s, splits, kchunk, ws);
     }
-    return launch_k4_orient<1, 1, 1, 1, 16, false, 4, false, 2, 4>(g, s, splits, kchunk, ws);
+    return launch_k4_orient<1, 1, 1, 1, 16, false, 4, false, 2, 4, true, 4, 2, false, false, true>(g, s, splits, kchunk, ws);
 }
 
 // 16-byte loads only (the plan never picks it otherwise: with 4-byte loads
