@@ -24,7 +24,11 @@
 //           each) followed by a gap of GAP bytes.  The two halves of a wave
 //           read rows k and k + BK/2 in the same instruction; the gap puts
 //           them 128 bytes apart modulo 256, on disjoint halves of the 64
-//           banks.  A lane reads single floats.
+//           banks.  A lane reads single floats, or with WIDE eight bytes
+//           (two interleaved columns, below), where the gap is doubled: an
+//           8-byte read serves 32 lanes at a time, two k-slot groups of 16
+//           lanes each covering 128 contiguous bytes, which the doubled gap
+//           puts on disjoint halves of the banks.
 //
 // Loads (global -> LDS, direct): each load instruction moves 64 lanes x LSIZE
 // bytes (16 with VEC, else 4) into a contiguous run of LDS; instruction u of
@@ -40,11 +44,14 @@
 // groups' rows on disjoint quarters of the banks (16-column runs).
 //
 // Columns of a wave's accumulator blocks: block nb's column j (the lane's
-// L%32) is tile column wn*TN*32 + nb*32 + j, except with B stored K x N and
-// TN = 4 (B_INTERLEAVE), where it is wn*TN*32 + 4*j + nb: the four blocks
-// interleave, so a lane's four B values of one k are 16 contiguous bytes of
-// a KRows row (one ds_read_b128) and its four outputs of one row are 16
-// contiguous bytes of C.
+// L%BLK) is tile column wn*TN*32 + nb*BLK + j, except with B stored K x N
+// and NB = 4 blocks (TN = 4, or TN = 2 with MF16) or MF16 with NB = 2
+// (B_INTERLEAVE), where it is wn*TN*32 + NB*j + nb: the blocks interleave,
+// so a lane's NB values of B of one k are 4*NB contiguous bytes of a KRows
+// row (one ds_read_b128 or ds_read_b64) and its NB outputs of one row are
+// 4*NB contiguous bytes of C.  (Without it, the compiler pairs the 16 x 16
+// blocks' single-float reads into ds_read2_b32, whose two accesses per lane
+// overlap the next k-slot group's banks: 25 % of LDS accesses conflicted.)
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -79,7 +86,7 @@ struct KMajor {
     }
 };
 
-template <int COLS_, int BK_, bool VEC_>
+template <int COLS_, int BK_, bool VEC_, bool WIDE_ = false>
 struct KRows {
     static constexpr int COLS = COLS_, BK = BK_;
     static constexpr bool KMAJOR = false;
@@ -87,7 +94,7 @@ struct KRows {
     static constexpr int ROW = COLS * 4;
     static constexpr int RPB = 1024 / ROW;
     static constexpr int BLOCKS = BK / RPB;
-    static constexpr int GAP = 128 * 2 * RPB / BK;
+    static constexpr int GAP = (WIDE_ ? 2 : 1) * 128 * 2 * RPB / BK;
     static constexpr int STRIDE = 1024 + GAP;
     static constexpr int STAGE = BLOCKS * STRIDE;
     static constexpr int INSTR = BK * ROW / IB;
@@ -138,8 +145,10 @@ struct Cfg {
     static constexpr int NWAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * NWAVES;
     static constexpr int BM = WAVES_M * TM * 32, BN = WAVES_N * TN * 32;
+    static constexpr bool B_INTERLEAVE = !B_KMAJOR && (MF16 ? (NB == 2 || NB == 4) : TN == 4);
     using LA = typename pick<A_KMAJOR, KMajor<BM, BK, VEC>, KRows<BM, BK, VEC>>::type;
-    using LB = typename pick<B_KMAJOR, KMajor<BN, BK, VEC>, KRows<BN, BK, VEC>>::type;
+    using LB = typename pick<B_KMAJOR, KMajor<BN, BK, VEC>,
+                             KRows<BN, BK, VEC, MF16 && B_INTERLEAVE && NB == 2>>::type;
     static constexpr int A_BASE = 0, B_BASE = LA::STAGE;
     static constexpr int STAGE = LA::STAGE + LB::STAGE;
     static constexpr int LDS_BYTES = NSTAGE * STAGE;
@@ -151,14 +160,13 @@ struct Cfg {
     static_assert(LA::INSTR % NWAVES == 0 && LB::INSTR % NWAVES == 0, "loads split evenly over waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 
-    static constexpr bool B_INTERLEAVE = !B_KMAJOR && TN == 4 && !MF16;
     // Slab column that k-slot s stands for at MFMA step t.
     __host__ __device__ static constexpr int kslot(int s, int t) { return s * KH + t; }
     // Tile row and column of a wave's accumulator blocks (lane index
     // j = L % BLK).
     __host__ __device__ static constexpr int a_row(int wm, int mb, int j) { return wm * TM * 32 + mb * BLK + j; }
     __host__ __device__ static constexpr int b_col(int wn, int nb, int j) {
-        return B_INTERLEAVE ? wn * TN * 32 + 4 * j + nb : wn * TN * 32 + nb * BLK + j;
+        return B_INTERLEAVE ? wn * TN * 32 + NB * j + nb : wn * TN * 32 + nb * BLK + j;
     }
     // Row within its block of accumulator register r of a lane in k-slot
     // group s = L / BLK (its column is L % BLK).

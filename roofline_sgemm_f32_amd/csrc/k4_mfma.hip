@@ -44,6 +44,7 @@
 namespace sgemm {
 
 namespace {
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -286,12 +287,17 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                     }
                 }
                 if constexpr (CF::B_INTERLEAVE) {
-                    // The lane's four columns of one k: one 16-byte read.
+                    // The lane's NB columns of one k: one 16- or 8-byte read.
+                    using BV = typename std::conditional<NB == 4, v4f, v2f>::type;
+                    static_assert(NB == 4 || NB == 2, "interleaved columns");
 #pragma unroll
                     for (int u = 0; u < KP; u++) {
-                        const v4f v = *(const v4f*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), CF::b_col(wn, 0, li)));
+                        const BV v = *(const BV*)(st + CF::b_elem(CF::kslot(ls, h * KP + u), CF::b_col(wn, 0, li)));
 #pragma unroll
                         for (int nb = 0; nb < NB; nb++) bf[nb][u] = v[nb];
+                        // Keep 8-byte reads single: paired into ds_read2_b64,
+                        // a lane's two rows would fall on the same banks.
+                        if constexpr (NB == 2) asm volatile("" ::: "memory");
                     }
                 } else {
 #pragma unroll
@@ -483,29 +489,30 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         // is nonzero; C is not read otherwise).
         const bool interior = tile_inside;
         if constexpr (CF::B_INTERLEAVE) {
-            // A lane's four blocks hold four neighbouring columns of each of
-            // its rows: 16-byte stores (and loads of C when beta is nonzero)
-            // where C allows.  Interleaved columns with 4-byte stores wrote
-            // partial cache lines and cost 6 % at square 4096; with these, the
-            // interleave measured square 4096 0.959 -> 0.948 ms, 8192 7.61 ->
-            // 7.52, 5632 2.62 -> 2.59 on MI355X (one 16-byte LDS read per k
-            // step in place of two two-float reads).
+            // A lane's NB blocks hold NB neighbouring columns of each of its
+            // rows: 16- or 8-byte stores (and loads of C when beta is
+            // nonzero) where C allows.  Interleaved columns with 4-byte
+            // stores wrote partial cache lines and cost 6 % at square 4096;
+            // with these, the interleave measured square 4096 0.959 -> 0.948
+            // ms, 8192 7.61 -> 7.52, 5632 2.62 -> 2.59 on MI355X (one 16-byte
+            // LDS read per k step in place of two two-float reads).
+            using CV = typename std::conditional<NB == 4, v4f, v2f>::type;
             const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
             if (interior && vec_c) {
 #pragma unroll
                 for (int mb = 0; mb < MB; mb++) {
-                    const int rbase = row0 + CF::a_row(wm, mb, 0) + ls * 4;
+                    const int rbase = row0 + CF::a_row(wm, mb, 0) + CF::acc_row(ls, 0);
                     float* cp = C + (int64_t)rbase * ldc + col0 + CF::b_col(wn, 0, li);
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        v4f* d = (v4f*)(cp + (int64_t)((r / 4) * 8 + (r % 4)) * ldc);
-                        v4f v;
+                    for (int r = 0; r < NREG; r++) {
+                        CV* d = (CV*)(cp + (int64_t)CF::acc_row(0, r) * ldc);
+                        CV v;
 #pragma unroll
-                        for (int nb = 0; nb < 4; nb++) v[nb] = alpha * acc[mb][nb][r];
+                        for (int nb = 0; nb < NB; nb++) v[nb] = alpha * acc[mb][nb][r];
                         if (read_c) {
-                            const v4f c0 = *d;
+                            const CV c0 = *d;
 #pragma unroll
-                            for (int nb = 0; nb < 4; nb++) v[nb] = fmaf(beta, c0[nb], v[nb]);
+                            for (int nb = 0; nb < NB; nb++) v[nb] = fmaf(beta, c0[nb], v[nb]);
                         }
                         if constexpr (SPLITK) *d = v;
                         else __builtin_nontemporal_store(v, d);

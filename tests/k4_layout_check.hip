@@ -50,24 +50,26 @@ void check_frags(const char* name) {
                 return IS_A ? CF::a_row(w, blk, l % CF::BLK) : CF::b_col(w, blk, l % CF::BLK);
             };
             if constexpr (!IS_A && CF::B_INTERLEAVE) {
-                // One ds_read_b128 per k step covers the lane's four blocks:
-                // 16-byte aligned, the four columns contiguous, 16 lanes per
-                // 256-byte bank window.
+                // One read per k step covers the lane's NB blocks: 4 NB
+                // bytes, aligned and contiguous.  The LDS serves 256 / (4 NB)
+                // consecutive lanes at a time (16 for ds_read_b128, 32 for
+                // ds_read_b64); those lanes must touch distinct banks.
                 if (blk != 0) continue;
+                constexpr int W = 4 * CF::NB, PER = 256 / W;
                 for (int t = 0; t < CF::KH; t++)
-                    for (int g = 0; g < 4; g++) {
-                        std::vector<int> slot(16, 0);
-                        for (int l = 16 * g; l < 16 * g + 16; l++) {
-                            const int k = CF::kslot(l >> 5, t);
-                            const int off = CF::b_elem(k, CF::b_col(w, 0, l & 31));
-                            CHECK(off % 16 == 0, "%s interleaved b128 misaligned", name);
-                            for (int e = 1; e < 4; e++)
-                                CHECK(CF::b_elem(k, CF::b_col(w, e, l & 31)) == off + 4 * e,
-                                      "%s interleaved b128 not contiguous", name);
-                            slot[(off / 16) % 16]++;
+                    for (int g = 0; g < 64 / PER; g++) {
+                        std::vector<int> bank(64, 0);
+                        for (int l = PER * g; l < PER * g + PER; l++) {
+                            const int k = CF::kslot(l / CF::BLK, t);
+                            const int off = CF::b_elem(k, CF::b_col(w, 0, l % CF::BLK));
+                            CHECK(off % W == 0, "%s interleaved read misaligned", name);
+                            for (int e = 1; e < CF::NB; e++)
+                                CHECK(CF::b_elem(k, CF::b_col(w, e, l % CF::BLK)) == off + 4 * e,
+                                      "%s interleaved read not contiguous", name);
+                            for (int e = 0; e < CF::NB; e++) bank[(off / 4 + e) % 64]++;
                         }
-                        for (int s = 0; s < 16; s++)
-                            CHECK(slot[s] <= 1, "%s interleaved b128 bank conflict w=%d t=%d g=%d", name, w, t, g);
+                        for (int b = 0; b < 64; b++)
+                            CHECK(bank[b] <= 1, "%s interleaved read bank conflict w=%d t=%d g=%d", name, w, t, g);
                     }
             } else if constexpr (KM) {
                 for (int q = 0; q < CF::KH / 4; q++)
