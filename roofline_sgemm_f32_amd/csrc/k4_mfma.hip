@@ -782,6 +782,9 @@ hipError_t launch_k4_t32_wk4(const GemmArgs& g, hipStream_t s, int splits, int k
     if (vec_ok(g)) {
         const int64_t share = (splits > 1 ? kchunk : g.K) / 4;
         const int64_t wgs = ceil_div(g.M, 32) * ceil_div(g.N, 32) * (splits > 1 ? splits : 1);
+        // More than three per CU: slabs of 16 in two stages, four per CU.
+        if (wgs > 3 * 256)
+            return launch_k4_orient<1, 1, 1, 1, 16, true, 4, true, 2, 4, true, 4, 2, false, true, true>(g, s, splits, kchunk, ws);
         if (share <= 256)
             return launch_k4_orient<1, 1, 1, 1, 16, true, 3, true, 3, 4, true, 2, 2, false, true, true>(g, s, splits, kchunk, ws);
         if (wgs >= 2 * 256)

@@ -43,9 +43,13 @@ namespace sgemm {
 //    third bound on K x tiles that no other shape supports, and the rule's
 //    gains elsewhere are 5-20 %, so it keeps them.  On packed
 //    copies only up to K = 1024 (800 x 801 x 2047 41.5 us split on 64 x 64
-//    tiles against 43.8); with 784 or more tiles (896^3 21.3 -> 24.0, 1024^3
-//    23.7 -> 26.6) or longer K (512 x 768 x 4096 35.9 -> 44.3) the 64 x 64
-//    choice stays.
+//    tiles against 43.8); with longer K (512 x 768 x 4096 35.9 -> 44.3) the
+//    64 x 64 choice stays.  From 769 to 1024 tiles these run four per CU
+//    with slabs of 16 in two stages (one round), once K groups of one wave
+//    ran without per-slab barriers: square 1024 23.2 -> 21.9 us, 896^3 19.0
+//    -> 18.4, 800 x 1024 x 1024 22.9 -> 20.2, 1024^2 x 2048 39.9 -> 39.4
+//    (earlier, with barriers and three per CU in two rounds, 896^3 21.3 ->
+//    24.0 and 1024^3 23.7 -> 26.6 against 64 x 64 tiles).
 //  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
 //    SIMD, fragments read in halves, raised wave priority during the
 //    matrix instructions) when the tiles fill whole rounds of 2 per CU, or
@@ -139,7 +143,7 @@ SplitPlan k4_plan(const GemmArgs& g, int requested) {
     } else if (T64 >= 512 || (vec && T64 > 256 && T32 > 256)) {
         cfg = K4_T64;
         tiles = T64;
-    } else if (T32 <= 256 || !vec || (T32 <= 3 * kCUs && g.K <= (g.runs_padded ? 1024 : 2048))) {
+    } else if (T32 <= 256 || !vec || (T32 <= 4 * kCUs && g.K <= (g.runs_padded ? 1024 : 2048))) {
         cfg = K4_T32_WK4;
         tiles = T32;
     } else {

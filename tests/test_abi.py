@@ -273,13 +273,15 @@ def test_plan_config_choices(lib):
         assert cfg(4096, 4096, 4096, transa=ta, transb=tb, lda=4096, ldb=4096)["tile"] == (128, 256)
     assert cfg(6144, 6144, 6144)["tile"] == (128, 128)               # 2.25 rounds of 128 x 256
     assert cfg(3072, 3072, 3072)["tile"] == (64, 64)
-    assert cfg(1024, 1024, 1024)["tile"] == (64, 64) and cfg(1024, 1024, 1024)["k_groups"] == 4
     small = cfg(256, 256, 256)
     assert small["tile"] == (32, 32) and small["k_groups"] == 4 and small["splits"] == 1
-    # Up to 768 such tiles with K <= 2048: one round of three workgroups per CU.
-    mid = cfg(640, 640, 640)
-    assert mid["tile"] == (32, 32) and mid["k_groups"] == 4 and mid["splits"] == 1
-    assert cfg(896, 896, 896)["tile"] == (64, 64)     # 784 tiles of 32 x 32
+    # Up to 1024 such tiles with K <= 2048: one round of three (up to 768
+    # tiles) or four workgroups per CU.
+    for M, N, K in [(640, 640, 640), (896, 896, 896), (1024, 1024, 1024), (1024, 1024, 2048)]:
+        mid = cfg(M, N, K)
+        assert mid["tile"] == (32, 32) and mid["k_groups"] == 4 and mid["splits"] == 1, (M, N, K, mid)
+    assert cfg(1024, 1024, 4096)["tile"] == (64, 64) and cfg(1024, 1024, 4096)["k_groups"] == 4
+    assert cfg(1056, 1024, 1024)["tile"] == (64, 64)  # 1056 tiles of 32 x 32
     assert cfg(640, 640, 4096)["tile"] == (64, 64)    # a longer K
     assert cfg(128, 128, 4096)["splits"] == 16
     skinny = cfg(64, 8192, 8192)

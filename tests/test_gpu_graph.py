@@ -27,7 +27,8 @@ def gpu():
 
 
 # (shape, what the eager AUTO call would do)
-CASES = [((1024, 1024, 1024), "64x64 tiles with K groups"),
+CASES = [((1024, 1024, 1024), "32x32 tiles with K groups, four workgroups per CU"),
+         ((1024, 1024, 4096), "64x64 tiles with K groups"),
          ((4096, 4096, 1024), "128x256 tiles"),
          ((128, 128, 4096), "split-K when eager"),
          ((1601, 1283, 97), "packed operands when eager"),

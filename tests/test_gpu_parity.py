@@ -279,12 +279,14 @@ def test_thin_unaligned_auto(shape):
     full_check("auto", M, N, K, "int", seed=M + K)
 
 
-# Mid-size outputs of 257 to 768 tiles of 32 x 32 with K <= 2048, which the
+# Mid-size outputs of 257 to 1024 tiles of 32 x 32 with K <= 2048, which the
 # plan runs unsplit on 32 x 32 tiles with 4 K groups (K slabs of 16 in three
-# LDS stages, or of 32 in two); edges that are not tile multiples included,
-# and K from 640 to 2048.
+# LDS stages, or of 32 in two; more than 768 tiles: slabs of 16 in two
+# stages, four workgroups per CU); edges that are not tile multiples
+# included, and K from 640 to 2048.
 MID = [(640, 640, 640), (300, 1000, 900), (768, 1024, 1024), (1000, 700, 1000),
-       (768, 1024, 1280), (1024, 768, 2048), (512, 768, 2048), (700, 900, 1500)]
+       (768, 1024, 1280), (1024, 768, 2048), (512, 768, 2048), (700, 900, 1500),
+       (896, 896, 896), (1000, 1000, 1024), (800, 1024, 2048)]
 
 
 @pytest.mark.parametrize("shape", MID, ids=lambda s: "x".join(map(str, s)))
