@@ -723,12 +723,15 @@ bool vec_ok(const GemmArgs& g) {
 
 hipError_t launch_k4_tile128x256(const GemmArgs& g, hipStream_t s) {
     using k4::Cfg;
-    // With the pipelined slab, raised wave priority helps only with B stored
-    // N x K (square 4096 933 -> 945 us without it); as stored it now costs
-    // 0.3-0.5 % (square 4096 929 -> 926 us, 8192 7.346 -> 7.316 ms, 5632
-    // 2.541 -> 2.533 ms), with A stored K x M 1 % (952 -> 942 us).
+    // Raised wave priority with the pipelined slab: with A stored K x M it
+    // costs 1 % (952 -> 942 us without it) and is off.  As stored it costs
+    // 0.3 % (square 4096 929 against 926 us, 8192 7.346 against 7.316 ms) but
+    // keeps the two workgroups of a CU in step: without it the L2 misses of
+    // square 4096 rise from 388 to 600 MB per launch (FETCH_SIZE), re-reads
+    // the Infinity Cache absorbs there and HBM would not at larger sizes.
+    // With B stored N x K it is 1.3 % faster (933 against 945 us).
     if (vec_ok(g)) {
-        if (!g.trans_a && !g.trans_b) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, true, false>, 2, true, 1, false, 2, true>(g, s);
+        if (!g.trans_a && !g.trans_b) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, true, false>, 2, true, 1, true, 2, true>(g, s);
         if (!g.trans_a) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, true, true>, 2, true, 1, true, 2, true>(g, s);
         if (!g.trans_b) return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, false, false>, 2, true, 1, false, 2, true>(g, s);
         return launch_k4_cfg<Cfg<2, 2, 2, 4, 16, true, false, true>, 2, true, 1, true, 2, true>(g, s);

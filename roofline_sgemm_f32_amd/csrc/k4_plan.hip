@@ -51,9 +51,9 @@ namespace sgemm {
 //    (earlier, with barriers and three per CU in two rounds, 896^3 21.3 ->
 //    24.0 and 1024^3 23.7 -> 26.6 against 64 x 64 tiles).
 //  * T128x256: 128 x 256 tiles (4 waves of 2 x 4 accumulators, 2 waves per
-//    SIMD, fragments read in halves; with B stored N x K raised wave
-//    priority during the matrix instructions) when the tiles fill whole
-//    rounds of 2 per CU, or
+//    SIMD, fragments read in halves, raised wave priority during the
+//    matrix instructions except with A stored K x M) when the tiles fill
+//    whole rounds of 2 per CU, or
 //    the last round at least 3/4: square 4096 0.956 ms against 0.990 on
 //    128 x 128, 8192 7.57 against 7.79 ms, 5632 2.63 against 2.71; with a
 //    smaller last round (square 3072, 4608, 6144) it is the slowest of the
