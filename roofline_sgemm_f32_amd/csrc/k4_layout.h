@@ -30,6 +30,18 @@
 //           lanes each covering 128 contiguous bytes, which the doubled gap
 //           puts on disjoint halves of the banks.
 //
+// 16-byte reads (measured on MI355X with SQ_LDS_BANK_CONFLICT): half a wave
+// is served in two passes when its lanes L and L + 16 read the same bank
+// positions (address modulo 256) and its first 16 lanes 16 distinct ones, in
+// four passes otherwise.  The 32 x 32 instruction's reads meet this (lanes L
+// and L + 16 read rows 16 apart, or one contiguous 512-byte run); the 16 x 16
+// one's do not (lanes L and L + 16 read the same row at the next k-slot),
+// and its 16-byte reads of KMajor images and of four interleaved columns
+// take four passes per half.  A layout that puts a row's chunks 256 bytes
+// apart fixes the reads but spreads each row over lanes 16 apart in every
+// load instruction, and measured no faster (square 3072 429 -> 436 us on
+// 64 x 64 tiles; square 6144 within 1 % on 128 x 128).
+//
 // Loads (global -> LDS, direct): each load instruction moves 64 lanes x LSIZE
 // bytes (16 with VEC, else 4) into a contiguous run of LDS; instruction u of
 // an operand's slab covers bytes [u*IB, (u+1)*IB) of its unpadded image,
