@@ -320,16 +320,33 @@ def compute_probe(valu_iters=4096, mfma_iters=4096, steps=30, warmup=10):
             "launches": steps}
 
 
+# Products up to this many multiply-adds are gated on every row of C, as far
+# as the rows of A checked hold at most ROW_GATE_A_ELEMS elements (evenly
+# spaced rows beyond that); larger products (the ladder rows at square4096)
+# on six rows.
+ROW_GATE_FULL_MACS = 2 ** 33
+ROW_GATE_A_ELEMS = 2 ** 24
+
+
 def row_gate(A_h, B_h):
     """Correctness gate for a timed GPU product outside the headline leg (a
-    ladder row, a small-shape plan): a few rows of C (first, last and some
-    between) against numpy's float64 product of the same host operands, with
-    the binary32 dot-product bound 4 K 2^-24 sum|a b| per element.  Its
-    throughput is printed only when the result passes."""
+    ladder row, a small-shape plan): the rows of C (all of them for products
+    of up to ROW_GATE_FULL_MACS multiply-adds and ROW_GATE_A_ELEMS elements
+    of A, evenly spaced ones up to that many elements for a larger A, else a
+    few: first, last and some between), against numpy's float64 product of
+    the same host operands, with the binary32 dot-product bound
+    4 K 2^-24 sum|a b| per element.  Its throughput is printed only when the
+    result passes."""
     import numpy as np
     from roofline_sgemm_f32_amd.inputs import as_numpy
     M, K = A_h.shape
-    rows = sorted({0, 1 % M, M // 3, M // 2, max(M - 2, 0), M - 1})
+    N = B_h.shape[1]
+    sentinel = {0, 1 % M, M // 3, M // 2, max(M - 2, 0), M - 1}
+    if M * N * K <= ROW_GATE_FULL_MACS:
+        n = max(1, min(M, ROW_GATE_A_ELEMS // max(K, 1)))
+        rows = sorted(sentinel | {i * M // n for i in range(n)})
+    else:
+        rows = sorted(sentinel)
     A64 = as_numpy(A_h)[rows].astype(np.float64)
     B64 = as_numpy(B_h).astype(np.float64)
     ref = A64 @ B64

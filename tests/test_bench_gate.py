@@ -51,6 +51,18 @@ def test_row_gate_single_row():
     assert bench.row_gate(A, B)(A @ B)[0]
 
 
+def test_row_gate_checks_every_row_of_small_products(monkeypatch):
+    """Up to ROW_GATE_FULL_MACS multiply-adds every row is gated: an error in
+    a row that is none of the six sampled ones fails; above the limit only
+    the sampled rows are."""
+    A, B = _operands(37, 29, 301, 16)
+    C = A @ B
+    C[7, 3] += 0.1        # row 7: not 0, 1, 12, 18, 35 or 36
+    assert bench.row_gate(A, B)(C)[0] is False
+    monkeypatch.setattr(bench, "ROW_GATE_FULL_MACS", 1)
+    assert bench.row_gate(A, B)(C)[0] is True
+
+
 def test_oracle_gate_checks_every_element():
     """bench.oracle_gate (the CPU leg's full-product gate): a float32 product
     passes, one wrong element anywhere fails."""
