@@ -266,7 +266,8 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         auto slab_step = [&](int s, auto check, auto whole) {
             const char* st = smem + ((s % NS) * WK + kg) * CF::STAGE;
             // Fragments are read and consumed in NH parts of KH / NH steps;
-            // with NH = 2 only half of them are live at a time.
+            // with NH = 2 the second part's reads are issued while the first
+            // part's MFMAs run.
             constexpr int NH = SPLIT ? 2 : 1, KP = KH / NH;
             static_assert(!(CF::A_KMAJOR || CF::B_KMAJOR) || KP % 4 == 0, "16-byte fragment reads");
             auto read_frags = [&](int h, float (&af)[MB][KP], float (&bf)[NB][KP]) {
@@ -390,11 +391,21 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                     }
                 }
                 if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
-                mfmas(af, bf);
-#pragma unroll
-                for (int h = 1; h < NH; h++) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    read_frags(h, af, bf);
+                if constexpr (NH == 2) {
+                    // The second half's reads after half of the first
+                    // half's MFMAs (into registers of their own): square
+                    // 3072 429 -> 425 us, 2048 130.9 -> 129.7, 4608 1.465 ->
+                    // 1.457 ms, 3001 x 4099 x 2047 422.5 -> 420.7 us on 64 x 64
+                    // tiles; right after the first MFMA step 3001 x 4099 x
+                    // 2047 took 438 us.
+                    float af1[MB][KP], bf1[NB][KP];
+                    mfmas(af, bf);
+                    read_frags(1, af1, bf1);
+                    mfmas(af1, bf1);
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF * KP / 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF * (2 * KP - KP / 2), 0);
+                } else {
                     mfmas(af, bf);
                 }
             }
