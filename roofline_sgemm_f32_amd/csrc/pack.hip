@@ -4,9 +4,10 @@
 // dimension per lane, so it needs 16-byte aligned rows and a row length
 // (the "run") that is a multiple of 4, or else rows padded with zeros up to
 // one.  pack_rows copies a stored rows x cols matrix (any alignment, any
-// leading dimension) into a dense rows x ld_dst one, ld_dst = cols rounded
-// up to 4, with the extra columns zero: a 16-byte chunk that straddles the
-// end of a row then reads zeros, whose products add exactly nothing.
+// leading dimension) into a dense rows x ld_dst one, ld_dst = packed_ld(cols)
+// (a multiple of 4), with the extra columns zero: a 16-byte chunk that
+// straddles the end of a row then reads zeros, whose products add exactly
+// nothing.
 #include <algorithm>
 
 #include "kernels.h"
@@ -56,7 +57,7 @@ __device__ __forceinline__ void pack_piece(const float* s, float* d, int64_t c0,
 __global__ void __launch_bounds__(256)
 pack_rows(PackJob j0, PackJob j1) {
     const PackJob j = blockIdx.y == 0 ? j0 : j1;
-    const int64_t ld_dst = (j.cols + 3) / 4 * 4;
+    const int64_t ld_dst = packed_ld(j.cols);
     if (ld_dst <= 2 * 256) {
         for (int64_t r = blockIdx.x; r < j.rows; r += gridDim.x) {
             const float* s = j.src + r * j.ld;
@@ -77,8 +78,6 @@ pack_rows(PackJob j0, PackJob j1) {
     }
 }
 }  // namespace
-
-int64_t packed_ld(int64_t cols) { return (cols + 3) / 4 * 4; }
 
 hipError_t launch_pack(const float* src, int64_t rows, int64_t cols, int64_t ld, float* dst,
                        const float* src2, int64_t rows2, int64_t cols2, int64_t ld2, float* dst2,
