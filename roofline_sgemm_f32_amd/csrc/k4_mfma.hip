@@ -468,7 +468,8 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
 #pragma unroll
                 for (int g = 1; g < WK; g++) sum[q] += *(const v4f*)(red + (g * CF::BM + row) * RLD + col);
             }
-            __syncthreads();  // the next tile's loads reuse this memory
+            // The next tile's loads reuse this memory (no next tile: no wait).
+            if (t + (int)gridDim.x < tiles) __syncthreads();
             const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
 #pragma unroll
             for (int q = 0; q < PER_LANE / 4; q++) {
