@@ -96,8 +96,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base) {
 // M x N slab z of the workspace passed as C (row stride ldc).
 // WK: the workgroup holds WK groups of CF's waves over the same tile; group g
 // takes slabs g, g + WK, g + 2 WK, ... in LDS stages of its own, and the
-// groups' accumulators are added through LDS (group order) before group 0
-// stores the tile.  This shortens each wave's chain of dependent MFMAs by
+// groups' accumulators are added through LDS (group order) by every lane of
+// the workgroup, which then stores the tile.  This shortens each wave's chain of dependent MFMAs by
 // WK without scratch memory or a second launch.
 // UNCHK: how a tile inside C issues the loads of whole slabs: 0 checked
 // like every other slab, 1 unchecked behind a branch per slab, 2 unchecked
@@ -351,9 +351,9 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                 // start, and the loads no longer delay the first MFMA.
                 // Measured on MI355X against the unpipelined slab (second
                 // half read after the first half's MFMAs, loads before them):
-                // square 4096 951 -> 939 us, 8192 7.55 -> 7.45 ms, 5632
-                // 2.60 -> 2.56 ms; with every read and load issued before
-                // the MFMAs, or the loads one per MFMA step, no gain.
+                // square 4096 940.5 -> 925.0 us, 8192 7.484 -> 7.329 ms, with
+                // A stored K x M 959.8 -> 946.6 us; with every read and load
+                // issued before the MFMAs, or one load per MFMA step, no gain.
                 float af[MB][KP], bf[NB][KP], af1[MB][KP], bf1[NB][KP];
                 if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
                 read_frags(0, af, bf);
