@@ -500,6 +500,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
         // column L % BLK of its block.  C = alpha * acc (+ beta * C when beta
         // is nonzero; C is not read otherwise).
         const bool interior = tile_inside;
+        const bool rows_aligned = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
         if constexpr (CF::B_INTERLEAVE) {
             // A lane's NB blocks hold NB neighbouring columns of each of its
             // rows: 16- or 8-byte stores (and loads of C when beta is
@@ -509,8 +510,7 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
             // ms, 8192 7.61 -> 7.52, 5632 2.62 -> 2.59 on MI355X (one 16-byte
             // LDS read per k step in place of two two-float reads).
             using CV = typename std::conditional<NB == 4, v4f, v2f>::type;
-            const bool vec_c = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && (ldc & 3) == 0;
-            if (interior && vec_c) {
+            if (interior && rows_aligned) {
 #pragma unroll
                 for (int mb = 0; mb < MB; mb++) {
                     const int rbase = row0 + CF::a_row(wm, mb, 0) + CF::acc_row(ls, 0);
@@ -543,11 +543,15 @@ k4_mfma(int M, int N, int K, const float* __restrict__ A, int lda, const float* 
                 if (interior && !read_c) {
                     // The final C goes out with non-temporal stores (0.1-0.8 %
                     // faster on unsplit products); split partial tiles, which
-                    // the reduction reads right back, keep the default policy.
+                    // the reduction reads right back, keep the default policy,
+                    // and so do rows that are not 16-byte aligned: their
+                    // single-float stores then merge into whole lines in the
+                    // L2 (3001 x 4099 x 2047: 52 MB written per product, C
+                    // being 49 MB, against 128 MB non-temporal; 420 -> 418 us).
 #pragma unroll
                     for (int r = 0; r < NREG; r++) {
                         float* d = cp + (int64_t)(CF::acc_row(0, r)) * ldc;
-                        if constexpr (SPLITK) *d = alpha * acc[mb][nb][r];
+                        if (SPLITK || !rows_aligned) *d = alpha * acc[mb][nb][r];
                         else __builtin_nontemporal_store(alpha * acc[mb][nb][r], d);
                     }
                 } else if (c < N) {
